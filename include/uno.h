@@ -1,0 +1,188 @@
+/*
+ * uno.h -- C ABI of the MI355X (gfx950) hot path of Uno (Psi-Spec) block
+ * draft-and-verify decoding.
+ *
+ * Sources of the operations (page titles as headed on the pages):
+ *  - "LoopUno: Turning Agentic Looped LLMs into Diffusion LLMs in One Hour",
+ *    section "How it works": a block of positions is drafted in one forward with
+ *    a LoRA that is switched on only for noise positions; the unmodified model
+ *    verifies them and the longest correct prefix is kept; the first position is
+ *    always the exact autoregressive token. Training is self-distillation with a
+ *    total-variation loss, and lossless acceptance equals 1 - TV.
+ *  - Same page, "Setup / Recipe": gated LoRA r = 128, alpha = 2048 on all seven
+ *    projections, noise rows only.
+ *  - "Uno Qwen3-8B" model card: the adapter is applied only to draft-noise rows;
+ *    seed, prefill, verification and AR rows use the frozen weights. Its
+ *    "Evaluation protocol" table fixes T = 1.0, top-p 0.95, top-k 50, block 16.
+ *
+ * Conventions shared by every call:
+ *  - Every tensor pointer is DEVICE memory owned by the caller. The library never
+ *    frees caller memory and keeps no per-call state between calls other than the
+ *    caller-provided workspace.
+ *  - All work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *    default stream) and runs asynchronously; results are valid after the caller
+ *    synchronises the stream.
+ *  - Argument errors are detected on the host before anything is launched; the
+ *    call then returns a non-zero uno_status and uno_last_error() holds a
+ *    message. A launch failure returns UNO_ERR_HIP. Nothing is thrown across the
+ *    ABI.
+ *  - Rows are contiguous (row-major, no padding). 16-byte aligned rows take the
+ *    vectorised path; other alignments are handled by a scalar path.
+ *  - Calls on different streams with different workspaces may run concurrently.
+ */
+#ifndef UNO_H
+#define UNO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  UNO_OK = 0,
+  UNO_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, out-of-range parameter */
+  UNO_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement            */
+  UNO_ERR_WORKSPACE = 3,     /* workspace missing or smaller than *_workspace() says   */
+  UNO_ERR_HIP = 4            /* a HIP runtime call failed (message in uno_last_error)  */
+} uno_status;
+
+typedef enum { UNO_DTYPE_F32 = 0, UNO_DTYPE_BF16 = 1 } uno_dtype;
+
+/* Sampling settings ("Uno Qwen3-8B" model card, "Evaluation protocol" table).
+ *   temperature <= 0  -> greedy (one-hot at the argmax, lowest id on ties)
+ *   top_k <= 0 or >= V -> top-k off; otherwise tie-inclusive: keep v iff z_v is
+ *                        >= the k-th largest logit counted with multiplicity
+ *   top_p >= 1        -> top-p off; otherwise tie-grouped: keep v iff the mass of
+ *                        strictly more probable tokens is < top_p (0 < top_p)
+ *   seed              -> Philox-4x64-10 key word 0 (key word 1 is the sequence id)
+ * temperature and top_p are doubles because the filtered-set arithmetic runs in
+ * fp64: the top-p comparison uses exactly the value the caller passes. */
+typedef struct {
+  double temperature;
+  double top_p;
+  int32_t top_k;
+  uint64_t seed;
+} uno_sampling_params;
+
+/* Bits of the per-slot flag word written to diag[..., 3] (as a float). */
+#define UNO_FLAG_TIE_ACCEPT 1      /* |u_acc - p~(d)/q~(d)| < 1e-6                          */
+#define UNO_FLAG_TIE_TOPP_P 2      /* a base-row top-p group boundary within 1e-6 of top_p  */
+#define UNO_FLAG_TIE_TOPP_Q 4      /* a draft-row top-p group boundary within 1e-6 of top_p */
+#define UNO_FLAG_TIE_ICDF 8        /* the inverse-CDF draw lies within 1e-6*Z of a boundary */
+#define UNO_FLAG_Q_ZERO 16         /* draft token outside supp(q~): rejected                */
+#define UNO_FLAG_RES_ZERO 32       /* residual mass zero after a rejection: drew from p~    */
+#define UNO_FLAG_OVERFLOW 64       /* a row needed the full-row path (large tied support)   */
+
+/* Human-readable name of a status code (static storage). */
+const char* uno_status_string(int status);
+/* Detail of the last error returned on this thread (static per-thread storage). */
+const char* uno_last_error(void);
+/* ABI version of this library (major * 100 + minor). */
+int uno_abi_version(void);
+
+/* Fill `bytes` of device memory with zeros on `stream` (a fill kernel, safe to
+ * record in a HIP graph). Every workspace must be zeroed once before its first
+ * use; each call leaves it zeroed again for the next call. */
+int uno_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Lossless block verification ("LoopUno", "How it works").
+ *
+ * For each sequence s and slot i of a block of b positions, p = filter(p_logits
+ * [s,i]) and q = filter(q_logits[s,i]) (temperature, then tie-inclusive top-k,
+ * then tie-grouped top-p on the renormalised top-k set, then renormalise).
+ *   slot 0      : the AR token, inverse CDF of p~ at u_res (q and draft ignored).
+ *   slot i >= 1 : accept draft d iff u_acc < p~(d)/q~(d); otherwise the slot's
+ *                 token is drawn from normalise(max(0, p~ - q~)) at u_res.
+ * accept_len[s] = first rejected slot (b if none, always >= 1). out_tokens[s,:]
+ * holds the kept tokens, then (if accept_len < b) the resampled token, then -1.
+ * Uniforms: Philox-4x64-10, key = (seed, seq_ids[s]), counter =
+ * (pos_offsets[s] + i, 0, 0, 0); word 0 -> u_acc, word 1 -> u_res, each as
+ * (w >> 40) * 2^-24. Filtered-set arithmetic runs in fp64; the top-k selection
+ * compares the input values exactly.
+ *
+ *   p_logits, q_logits : [S, b, V] of `dtype` (bf16 or fp32), contiguous
+ *   draft_tokens       : int32 [S, b]; slot 0 ignored
+ *   seq_ids, pos_offsets : int64 [S]
+ *   out_tokens         : int32 [S, b]  (out)
+ *   accept_len         : int32 [S]     (out) the tokens-per-forward numerator
+ *   resampled          : int32 [S]     (out) resampled token, -1 if all b kept
+ *   slot_accept        : uint8 [S, b]  (out, optional) raw per-slot decisions
+ *   diag               : float [S, b, 4] (out, optional) u_acc, p~(d)/q~(d), u_res,
+ *                        flag bits (UNO_FLAG_*)
+ *   workspace          : >= uno_verify_block_workspace(S, b, V) bytes, zeroed once
+ * Limits: 1 <= b <= 64, 1 <= V < 2^31, S >= 0 (S == 0 launches nothing).
+ * Rows whose filtered support is larger than 256 tokens, or top-k off / k > 256
+ * with V > 2048, are not handled by this build: their slot gets UNO_FLAG_OVERFLOW
+ * and token -1 (the call returns UNO_ERR_UNSUPPORTED up front when the settings
+ * alone make every row such a row).
+ * ------------------------------------------------------------------------- */
+size_t uno_verify_block_workspace(int S, int b, int V);
+int uno_verify_block(const void* p_logits, const void* q_logits, int dtype,
+                     const int32_t* draft_tokens, const int64_t* seq_ids,
+                     const int64_t* pos_offsets, int S, int b, int V,
+                     uno_sampling_params sp, int32_t* out_tokens, int32_t* accept_len,
+                     int32_t* resampled, uint8_t* slot_accept, float* diag,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Draft sampler: d[s,i] ~ filter(q_logits[s,i]) for every slot, by inverse CDF
+ * at Philox stream 1 (counter = (pos_offsets[s] + i, 1, 0, 0), word 0). This is
+ * the draft half of a Psi-Spec step ("LoopUno", "How it works": the block is
+ * drafted in one forward); its uniforms are independent of the verifier's.
+ *   q_logits : [S, b, V] of `dtype`; draft_tokens : int32 [S, b] (out)
+ *   flags    : int32 [S, b] (out, optional) UNO_FLAG_TIE_TOPP_Q / _TIE_ICDF /
+ *              _OVERFLOW
+ * Same limits as uno_verify_block; needs no workspace.
+ * ------------------------------------------------------------------------- */
+int uno_draft_sample(const void* q_logits, int dtype, const int64_t* seq_ids,
+                     const int64_t* pos_offsets, int S, int b, int V,
+                     uno_sampling_params sp, int32_t* draft_tokens, int32_t* flags,
+                     void* stream);
+
+/* ---------------------------------------------------------------------------
+ * TV self-distillation loss, forward and backward ("LoopUno", "How it works" ->
+ * "Training is self-distillation").
+ *   p = softmax(teacher/T), q = softmax(student/T) over the full vocabulary,
+ *   TV_r = 1/2 sum_v |p_v - q_v|, loss = sum_r mask_r TV_r / sum_r mask_r (0 if
+ *   no row is masked in), grad[r,j] = mask_r q_j (g_j - sum_v q_v g_v) /
+ *   (T * sum mask), g_v = 1/2 sign(q_v - p_v). The teacher gets no gradient.
+ *   teacher_logits, student_logits : [R, V] of `dtype`
+ *   response_mask : uint8 [R]
+ *   loss          : float [1] (out)
+ *   tv_rows       : float [R] (out, optional; 0 on masked-out rows)
+ *   grad_student  : [R, V] of `dtype` (out, optional; NULL = forward only)
+ *   workspace     : >= uno_tv_loss_workspace(R, V) bytes, zeroed once
+ * Limits: R >= 0, 1 <= V < 2^31, temperature > 0.
+ * ------------------------------------------------------------------------- */
+size_t uno_tv_loss_workspace(int R, int V);
+int uno_tv_loss_fwd_bwd(const void* teacher_logits, const void* student_logits, int dtype,
+                        const uint8_t* response_mask, int R, int V, float temperature,
+                        float* loss, float* tv_rows, void* grad_student,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Row-gated LoRA linear ("Uno Qwen3-8B" model card; "LoopUno", "Setup / Recipe"):
+ *   Y[m,n] = sum_k X[m,k] W[n,k] + scale * row_mask[m] * sum_j T[m,j] B[n,j],
+ *   T = X A^T (rank r), all bf16 in, fp32 accumulation, bf16 out (round to
+ *   nearest even). T is rounded to bf16 after scaling and gating.
+ *   X : bf16 [M, K]; W : bf16 [N, K] (nn.Linear layout); A : bf16 [r, K]
+ *   (lora_A); B : bf16 [N, r] (lora_B); row_mask : uint8 [M] (1 = noise row,
+ *   adapter on); Y : bf16 [M, N] (out, must not alias inputs)
+ *   workspace : >= uno_gated_lora_linear_workspace(M, N, K, r) bytes
+ * Limits: M, N, K >= 1, r >= 0 (r == 0: plain linear); K and r multiples of 8
+ * and all row starts 16-byte aligned (UNO_ERR_UNSUPPORTED otherwise).
+ * ------------------------------------------------------------------------- */
+size_t uno_gated_lora_linear_workspace(int M, int N, int K, int r);
+int uno_gated_lora_linear(const void* X, const void* W, const void* A, const void* B,
+                          const uint8_t* row_mask, float scale, void* Y,
+                          int M, int N, int K, int r,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UNO_H */

@@ -1,0 +1,183 @@
+// C ABI of libuno: argument validation, workspace sizing and kernel launch.
+// The operations and their contracts are documented in include/uno.h.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/uno.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return UNO_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(UNO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+uno::SamplingArgs to_args(const uno_sampling_params& sp) {
+  uno::SamplingArgs a;
+  a.temperature = sp.temperature;
+  a.top_p = sp.top_p;
+  a.top_k = sp.top_k;
+  a.seed = sp.seed;
+  return a;
+}
+
+// Shared checks of the verifier and the draft sampler.
+int check_sampling(const uno_sampling_params& sp, int S, int b, int V, const char* fn) {
+  if (S < 0) return fail(UNO_ERR_INVALID_ARG, "%s: S = %d < 0", fn, S);
+  if (b < 1 || b > 64) return fail(UNO_ERR_INVALID_ARG, "%s: block size b = %d outside [1, 64]", fn, b);
+  if (V < 1) return fail(UNO_ERR_INVALID_ARG, "%s: vocabulary V = %d < 1", fn, V);
+  if ((long long)S * b > 0x7fffffffLL)
+    return fail(UNO_ERR_INVALID_ARG, "%s: S * b = %lld slots exceeds 2^31 - 1", fn, (long long)S * b);
+  if (isnan(sp.temperature)) return fail(UNO_ERR_INVALID_ARG, "%s: temperature is NaN", fn);
+  if (!(sp.top_p > 0.0)) return fail(UNO_ERR_INVALID_ARG, "%s: top_p must be > 0 (got %g)", fn, sp.top_p);
+  const bool greedy = !(sp.temperature > 0.0);
+  const int k_eff = greedy ? 1 : ((sp.top_k > 0 && sp.top_k < V) ? sp.top_k : V);
+  if (k_eff > uno::kVerifyKMaxFast && V > uno::kVerifyCandCap)
+    return fail(UNO_ERR_UNSUPPORTED,
+                "%s: top-k %d (effective %d) over V = %d needs the full-row path, which this "
+                "build does not provide (single-pass selection handles k <= %d, or V <= %d)",
+                fn, sp.top_k, k_eff, V, uno::kVerifyKMaxFast, uno::kVerifyCandCap);
+  return UNO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* uno_status_string(int status) {
+  switch (status) {
+    case UNO_OK: return "UNO_OK";
+    case UNO_ERR_INVALID_ARG: return "UNO_ERR_INVALID_ARG";
+    case UNO_ERR_UNSUPPORTED: return "UNO_ERR_UNSUPPORTED";
+    case UNO_ERR_WORKSPACE: return "UNO_ERR_WORKSPACE";
+    case UNO_ERR_HIP: return "UNO_ERR_HIP";
+    default: return "UNO_ERR_UNKNOWN";
+  }
+}
+
+const char* uno_last_error(void) { return g_last_error; }
+
+int uno_abi_version(void) { return 100; }
+
+int uno_workspace_init(void* workspace, size_t bytes, void* stream) {
+  if (bytes == 0) return ok();
+  if (!workspace) return fail(UNO_ERR_INVALID_ARG, "uno_workspace_init: null workspace");
+  if (bytes % 4 != 0) return fail(UNO_ERR_INVALID_ARG, "uno_workspace_init: size %zu is not a multiple of 4", bytes);
+  return hip_status(uno::launch_zero(workspace, bytes, static_cast<hipStream_t>(stream)),
+                    "uno_workspace_init launch");
+}
+
+size_t uno_verify_block_workspace(int S, int b, int V) {
+  (void)V;
+  if (S <= 0 || b <= 0) return 256;
+  return uno::verify_workspace_bytes(S, b);
+}
+
+int uno_verify_block(const void* p_logits, const void* q_logits, int dtype,
+                     const int32_t* draft_tokens, const int64_t* seq_ids,
+                     const int64_t* pos_offsets, int S, int b, int V,
+                     uno_sampling_params sp, int32_t* out_tokens, int32_t* accept_len,
+                     int32_t* resampled, uint8_t* slot_accept, float* diag,
+                     void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "uno_verify_block";
+  int st = check_sampling(sp, S, b, V, fn);
+  if (st != UNO_OK) return st;
+  if (dtype != UNO_DTYPE_F32 && dtype != UNO_DTYPE_BF16)
+    return fail(UNO_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+  if (S == 0) return ok();
+  if (!p_logits || !q_logits || !draft_tokens || !seq_ids || !pos_offsets || !out_tokens ||
+      !accept_len || !resampled)
+    return fail(UNO_ERR_INVALID_ARG, "%s: a required pointer is null", fn);
+  const size_t need = uno_verify_block_workspace(S, b, V);
+  if (!workspace || ws_bytes < need)
+    return fail(UNO_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, need);
+  uno::VerifyArgs a;
+  a.p = p_logits;
+  a.q = q_logits;
+  a.bf16 = dtype == UNO_DTYPE_BF16;
+  a.draft = draft_tokens;
+  a.seq_ids = seq_ids;
+  a.pos = pos_offsets;
+  a.S = S;
+  a.b = b;
+  a.V = V;
+  a.sp = to_args(sp);
+  a.out_tokens = out_tokens;
+  a.accept_len = accept_len;
+  a.resampled = resampled;
+  a.slot_accept = slot_accept;
+  a.diag = diag;
+  a.ws = workspace;
+  return hip_status(uno::launch_verify(a, static_cast<hipStream_t>(stream)), "uno_verify_block launch");
+}
+
+int uno_draft_sample(const void* q_logits, int dtype, const int64_t* seq_ids,
+                     const int64_t* pos_offsets, int S, int b, int V,
+                     uno_sampling_params sp, int32_t* draft_tokens, int32_t* flags,
+                     void* stream) {
+  const char* fn = "uno_draft_sample";
+  int st = check_sampling(sp, S, b, V, fn);
+  if (st != UNO_OK) return st;
+  if (dtype != UNO_DTYPE_F32 && dtype != UNO_DTYPE_BF16)
+    return fail(UNO_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+  if (S == 0) return ok();
+  if (!q_logits || !seq_ids || !pos_offsets || !draft_tokens)
+    return fail(UNO_ERR_INVALID_ARG, "%s: a required pointer is null", fn);
+  uno::DraftArgs a;
+  a.q = q_logits;
+  a.bf16 = dtype == UNO_DTYPE_BF16;
+  a.seq_ids = seq_ids;
+  a.pos = pos_offsets;
+  a.S = S;
+  a.b = b;
+  a.V = V;
+  a.sp = to_args(sp);
+  a.draft = draft_tokens;
+  a.flags = flags;
+  return hip_status(uno::launch_draft(a, static_cast<hipStream_t>(stream)), "uno_draft_sample launch");
+}
+
+size_t uno_tv_loss_workspace(int R, int V) {
+  (void)R;
+  (void)V;
+  return 256;
+}
+
+int uno_tv_loss_fwd_bwd(const void*, const void*, int, const uint8_t*, int, int, float, float*,
+                        float*, void*, void*, size_t, void*) {
+  return fail(UNO_ERR_UNSUPPORTED, "uno_tv_loss_fwd_bwd: not built yet");
+}
+
+size_t uno_gated_lora_linear_workspace(int M, int N, int K, int r) {
+  (void)M;
+  (void)N;
+  (void)K;
+  (void)r;
+  return 256;
+}
+
+int uno_gated_lora_linear(const void*, const void*, const void*, const void*, const uint8_t*,
+                          float, void*, int, int, int, int, void*, size_t, void*) {
+  return fail(UNO_ERR_UNSUPPORTED, "uno_gated_lora_linear: not built yet");
+}
+
+}  // extern "C"

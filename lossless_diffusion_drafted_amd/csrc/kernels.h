@@ -1,0 +1,55 @@
+// Internal launch interface between the C ABI (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace uno {
+
+struct SamplingArgs {
+  double temperature;
+  double top_p;
+  int top_k;
+  uint64_t seed;
+};
+
+struct VerifyArgs {
+  const void* p;
+  const void* q;
+  bool bf16;
+  const int32_t* draft;
+  const int64_t* seq_ids;
+  const int64_t* pos;
+  int S, b, V;
+  SamplingArgs sp;
+  int32_t* out_tokens;
+  int32_t* accept_len;
+  int32_t* resampled;
+  uint8_t* slot_accept;
+  float* diag;
+  void* ws;
+};
+
+struct DraftArgs {
+  const void* q;
+  bool bf16;
+  const int64_t* seq_ids;
+  const int64_t* pos;
+  int S, b, V;
+  SamplingArgs sp;
+  int32_t* draft;
+  int32_t* flags;
+};
+
+// Largest top-k the single-pass selection handles, and largest vocabulary that
+// may be taken whole when top-k is off.
+constexpr int kVerifyKMaxFast = 256;
+constexpr int kVerifyCandCap = 2048;
+
+size_t verify_workspace_bytes(int S, int b);
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
+hipError_t launch_draft(const DraftArgs& a, hipStream_t stream);
+hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t stream);
+
+}  // namespace uno

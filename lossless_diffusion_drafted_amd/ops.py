@@ -1,0 +1,125 @@
+"""Python entry points with the C ABI's names (include/uno.h), over torch tensors.
+
+Each function validates shapes and dtypes, allocates outputs, and calls the
+library on the current HIP stream of the inputs' device. Results are
+asynchronous like any other work on that stream.
+"""
+
+import torch
+
+from . import _lib
+from ._lib import SamplingParams, WORKSPACES, check, load, ptr, require, stream_handle
+
+
+def sampling_params(temperature=1.0, top_k=50, top_p=0.95, seed=0):
+    return SamplingParams(float(temperature), float(top_p), int(top_k), int(seed) & (2**64 - 1))
+
+
+def uno_verify_block(p_logits, q_logits, draft_tokens, seq_ids, pos_offsets,
+                     temperature=1.0, top_k=50, top_p=0.95, seed=0,
+                     want_slot_accept=True, want_diag=True, out=None):
+    """Lossless verification of a [S, b, V] block (see uno_verify_block in uno.h).
+
+    Returns a dict of device tensors: out_tokens [S,b] int32, accept_len [S] int32,
+    resampled [S] int32, and optionally slot_accept [S,b] uint8, diag [S,b,4] f32.
+    `out` may pass preallocated tensors under the same keys.
+    """
+    lib = load()
+    if p_logits.dim() != 3:
+        raise ValueError("p_logits must be [S, b, V]")
+    S, b, V = p_logits.shape
+    dev = p_logits.device
+    require(p_logits, "p_logits")
+    require(q_logits, "q_logits", dtype=p_logits.dtype, shape=(S, b, V), device=dev)
+    require(draft_tokens, "draft_tokens", dtype=torch.int32, shape=(S, b), device=dev)
+    require(seq_ids, "seq_ids", dtype=torch.int64, shape=(S,), device=dev)
+    require(pos_offsets, "pos_offsets", dtype=torch.int64, shape=(S,), device=dev)
+    o = dict(out or {})
+    if "out_tokens" not in o:
+        o["out_tokens"] = torch.empty((S, b), dtype=torch.int32, device=dev)
+    if "accept_len" not in o:
+        o["accept_len"] = torch.empty((S,), dtype=torch.int32, device=dev)
+    if "resampled" not in o:
+        o["resampled"] = torch.empty((S,), dtype=torch.int32, device=dev)
+    if want_slot_accept and "slot_accept" not in o:
+        o["slot_accept"] = torch.empty((S, b), dtype=torch.uint8, device=dev)
+    if want_diag and "diag" not in o:
+        o["diag"] = torch.empty((S, b, 4), dtype=torch.float32, device=dev)
+    stream = stream_handle(dev)
+    nws = lib.uno_verify_block_workspace(S, b, V)
+    ws = WORKSPACES.get(dev, stream, "verify", nws)
+    sp = sampling_params(temperature, top_k, top_p, seed)
+    st = lib.uno_verify_block(ptr(p_logits), ptr(q_logits), _lib.dtype_code(p_logits),
+                              ptr(draft_tokens), ptr(seq_ids), ptr(pos_offsets), S, b, V, sp,
+                              ptr(o["out_tokens"]), ptr(o["accept_len"]), ptr(o["resampled"]),
+                              ptr(o.get("slot_accept")), ptr(o.get("diag")),
+                              ptr(ws), ws.numel(), stream)
+    check(st, "uno_verify_block")
+    return o
+
+
+def uno_draft_sample(q_logits, seq_ids, pos_offsets, temperature=1.0, top_k=50, top_p=0.95,
+                     seed=0, want_flags=True):
+    """Draft tokens d[s,i] ~ q~[s,i] (Philox stream 1). Returns (draft [S,b] int32, flags or None)."""
+    lib = load()
+    if q_logits.dim() != 3:
+        raise ValueError("q_logits must be [S, b, V]")
+    S, b, V = q_logits.shape
+    dev = q_logits.device
+    require(q_logits, "q_logits")
+    require(seq_ids, "seq_ids", dtype=torch.int64, shape=(S,), device=dev)
+    require(pos_offsets, "pos_offsets", dtype=torch.int64, shape=(S,), device=dev)
+    draft = torch.empty((S, b), dtype=torch.int32, device=dev)
+    flags = torch.empty((S, b), dtype=torch.int32, device=dev) if want_flags else None
+    sp = sampling_params(temperature, top_k, top_p, seed)
+    st = lib.uno_draft_sample(ptr(q_logits), _lib.dtype_code(q_logits), ptr(seq_ids),
+                              ptr(pos_offsets), S, b, V, sp, ptr(draft), ptr(flags),
+                              stream_handle(dev))
+    check(st, "uno_draft_sample")
+    return draft, flags
+
+
+def uno_tv_loss_fwd_bwd(teacher_logits, student_logits, response_mask, temperature=1.0,
+                        want_grad=True, want_rows=True):
+    """TV self-distillation loss and gradient. Returns (loss [1] f32, tv_rows or None, grad or None)."""
+    lib = load()
+    if teacher_logits.dim() != 2:
+        raise ValueError("teacher_logits must be [R, V]")
+    R, V = teacher_logits.shape
+    dev = teacher_logits.device
+    require(teacher_logits, "teacher_logits")
+    require(student_logits, "student_logits", dtype=teacher_logits.dtype, shape=(R, V), device=dev)
+    require(response_mask, "response_mask", dtype=torch.uint8, shape=(R,), device=dev)
+    loss = torch.empty((1,), dtype=torch.float32, device=dev)
+    rows = torch.empty((R,), dtype=torch.float32, device=dev) if want_rows else None
+    grad = torch.empty_like(student_logits) if want_grad else None
+    stream = stream_handle(dev)
+    ws = WORKSPACES.get(dev, stream, "tv", lib.uno_tv_loss_workspace(R, V))
+    st = lib.uno_tv_loss_fwd_bwd(ptr(teacher_logits), ptr(student_logits),
+                                 _lib.dtype_code(teacher_logits), ptr(response_mask), R, V,
+                                 float(temperature), ptr(loss), ptr(rows), ptr(grad),
+                                 ptr(ws), ws.numel(), stream)
+    check(st, "uno_tv_loss_fwd_bwd")
+    return loss, rows, grad
+
+
+def uno_gated_lora_linear(X, W, A, B, row_mask, scale=1.0, out=None):
+    """Y = X W^T + scale * row_mask * (X A^T) B^T in bf16 (see uno.h)."""
+    lib = load()
+    M, K = X.shape
+    N = W.shape[0]
+    r = A.shape[0]
+    dev = X.device
+    require(X, "X", dtype=torch.bfloat16)
+    require(W, "W", dtype=torch.bfloat16, shape=(N, K), device=dev)
+    require(A, "A", dtype=torch.bfloat16, shape=(r, K), device=dev)
+    require(B, "B", dtype=torch.bfloat16, shape=(N, r), device=dev)
+    require(row_mask, "row_mask", dtype=torch.uint8, shape=(M,), device=dev)
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    require(Y, "Y", dtype=torch.bfloat16, shape=(M, N), device=dev)
+    stream = stream_handle(dev)
+    ws = WORKSPACES.get(dev, stream, "gemm", lib.uno_gated_lora_linear_workspace(M, N, K, r))
+    st = lib.uno_gated_lora_linear(ptr(X), ptr(W), ptr(A), ptr(B), ptr(row_mask), float(scale),
+                                   ptr(Y), M, N, K, r, ptr(ws), ws.numel(), stream)
+    check(st, "uno_gated_lora_linear")
+    return Y

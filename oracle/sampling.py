@@ -132,7 +132,8 @@ def filter_logits(z, temperature, top_k, top_p):
             while g1 + 1 < n and zk[order[g1 + 1]] == zk[order[g0]]:
                 g1 += 1
             mass_above = above / z_top
-            gap = min(gap, abs(mass_above - top_p))
+            if not first:       # the top group is kept unconditionally: not a decision
+                gap = min(gap, abs(mass_above - top_p))
             if first or mass_above < top_p:
                 keep[order[g0:g1 + 1]] = True
             else:

@@ -1,0 +1,186 @@
+"""GPU parity of the HIP verifier and draft sampler against the CPU oracle.
+
+Token ids, accept lengths and resampled tokens must be bit-exact given the same
+Philox stream; a difference is tolerated only at a slot where either side flags
+a near-tie (|u - p~/q~| < 1e-6, a top-p boundary within 1e-6 of top_p, or an
+inverse-CDF draw within 1e-6*Z of a boundary), and such slots are counted.
+Draft tokens given to both sides come from the oracle's draft sampler; where a
+full-size workload is only sampled, the remaining sequences use the HIP draft
+sampler (their results are not compared).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import compare_verify, dtype_name, to_device
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+SP = workloads.SAMPLING
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import lossless_diffusion_drafted_amd as uno
+    uno.load()
+
+
+def _uno():
+    import lossless_diffusion_drafted_amd as uno
+    return uno
+
+
+def _gpu_verify(p, q, d, seq, pos, sp):
+    uno = _uno()
+    r = uno.uno_verify_block(to_device(p, DEV), to_device(q, DEV), to_device(d.astype(np.int32), DEV),
+                             to_device(seq, DEV), to_device(pos, DEV),
+                             temperature=sp["temperature"], top_k=sp["top_k"], top_p=sp["top_p"],
+                             seed=sp["seed"])
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in r.items()}
+
+
+def _run_full(p, q, sp, seq=None, pos=None):
+    S, b, V = p.shape
+    seq = np.arange(S, dtype=np.int64) if seq is None else seq
+    pos = np.zeros(S, dtype=np.int64) if pos is None else pos
+    dt = dtype_name(p)
+    d, _ = oracle.draft_sample(q, seq, pos, sp["temperature"], sp["top_k"], sp["top_p"], sp["seed"], dt)
+    ref = oracle.verify_block(p, q, d, seq, pos, sp["temperature"], sp["top_k"], sp["top_p"], sp["seed"], dt)
+    gpu = _gpu_verify(p, q, d, seq, pos, sp)
+    return compare_verify(gpu, ref, b), gpu, ref
+
+
+def test_draft_sampler_matches_oracle_tiny():
+    uno = _uno()
+    p, q = workloads.verify_logits("tiny")
+    S, b, V = q.shape
+    seq, pos = np.arange(S, dtype=np.int64), np.zeros(S, dtype=np.int64)
+    ref, rflags = oracle.draft_sample(q, seq, pos, SP["temperature"], SP["top_k"], SP["top_p"], SP["seed"], "f32")
+    d, flags = uno.uno_draft_sample(to_device(q, DEV), to_device(seq, DEV), to_device(pos, DEV), **SP)
+    torch.cuda.synchronize()
+    d, flags = d.cpu().numpy(), flags.cpu().numpy()
+    tie = (flags | rflags) & oracle.TIE_MASK
+    np.testing.assert_array_equal(d[tie == 0], ref[tie == 0])
+
+
+def test_verify_tiny():
+    p, q = workloads.verify_logits("tiny")
+    st, gpu, ref = _run_full(p, q, SP)
+    print("tiny", st, "accept_len", gpu["accept_len"])
+    assert st["exact"] == 1
+
+
+@pytest.mark.parametrize("V,S,b,seed", [(4096, 8, 16, 1), (32000, 4, 8, 2), (151936, 2, 16, 3)])
+def test_verify_qwen_distribution_reduced(V, S, b, seed):
+    cfg = dict(workloads.VERIFY_CONFIGS["qwen"], S=S, b=b)
+    p, q = workloads.verify_logits(cfg, seed=seed, V=V)
+    rng = np.random.default_rng(seed)
+    seq = rng.integers(0, 2**62, S, dtype=np.int64)
+    pos = rng.integers(0, 100000, S, dtype=np.int64)
+    st, gpu, ref = _run_full(p, q, SP, seq, pos)
+    print(V, S, b, st)
+    assert st["exact"] >= S - 1
+
+
+@pytest.mark.parametrize("V,b,k,top_p,T", [
+    (1, 4, 50, 0.95, 1.0), (7, 3, 50, 0.95, 1.0), (50, 8, 50, 0.95, 1.0), (51, 8, 50, 0.9, 1.0),
+    (1000, 1, 50, 0.95, 1.0), (4099, 5, 50, 0.95, 1.0), (2051, 64, 50, 0.5, 0.7),
+    (300, 6, 0, 1.0, 1.0), (2048, 4, 0, 0.95, 1.3), (3000, 4, 1, 0.95, 1.0),
+    (3000, 4, 50, 1e-9, 1.0), (3000, 6, 256, 0.99, 2.0), (5000, 6, 50, 0.95, 0.0),
+])
+def test_verify_ragged_and_settings(V, b, k, top_p, T):
+    S = 3
+    cfg = dict(workloads.VERIFY_CONFIGS["qwen"], S=S, b=b)
+    p, q = workloads.verify_logits(cfg, seed=V + b, V=V)
+    sp = dict(temperature=T, top_k=k, top_p=top_p, seed=11)
+    st, gpu, ref = _run_full(p, q, sp)
+    print(V, b, k, top_p, T, st)
+    assert st["exact"] + st["near_tie"] == S and st["exact"] >= S - 1
+
+
+def test_verify_fp32_unaligned_rows():
+    cfg = dict(workloads.VERIFY_CONFIGS["tiny"], S=3, b=5)
+    p, q = workloads.verify_logits(cfg, seed=4, V=1027)   # 1027*4 bytes: rows not 16-byte aligned
+    st, _, _ = _run_full(p, q, SP)
+    assert st["exact"] == 3
+
+
+def test_verify_many_ties():
+    rng = np.random.default_rng(5)
+    S, b, V = 4, 8, 3000
+    base = np.round(rng.normal(0, 3, (S, b, V)) * 2) / 2          # half-integer grid: heavy ties
+    p = workloads.to_bf16_bits(base.astype(np.float32))
+    q = workloads.to_bf16_bits((base + np.round(rng.normal(0, 1, (S, b, V)) * 2) / 2).astype(np.float32))
+    st, _, _ = _run_full(p, q, dict(SP, top_k=20))
+    assert st["exact"] + st["near_tie"] == S
+
+
+def test_verify_identical_rows_accept_everything():
+    p, _ = workloads.verify_logits(dict(workloads.VERIFY_CONFIGS["qwen"], S=4, b=16), V=8192)
+    st, gpu, _ = _run_full(p, p.copy(), SP)
+    assert np.all(gpu["accept_len"] == 16)
+
+
+def test_empty_batch_is_a_no_op():
+    uno = _uno()
+    z = torch.empty((0, 4, 100), dtype=torch.bfloat16, device=DEV)
+    r = uno.uno_verify_block(z, z, torch.empty((0, 4), dtype=torch.int32, device=DEV),
+                             torch.empty(0, dtype=torch.int64, device=DEV),
+                             torch.empty(0, dtype=torch.int64, device=DEV))
+    torch.cuda.synchronize()
+    assert r["accept_len"].numel() == 0
+
+
+@pytest.mark.parametrize("name,nsample", [("qwen", 6), ("looped", 6), ("stress", 4)])
+def test_verify_full_size_sampled(name, nsample):
+    """Full-size workload in the benchmark's launch configuration; the oracle checks a
+    seeded sample of sequences."""
+    uno = _uno()
+    c = workloads.VERIFY_CONFIGS[name]
+    S, b, V = c["S"], c["b"], c["V"]
+    p, q = workloads.verify_logits(name)
+    seq, pos = np.arange(S, dtype=np.int64), np.zeros(S, dtype=np.int64)
+    pd, qd = to_device(p, DEV), to_device(q, DEV)
+    dg, _ = uno.uno_draft_sample(qd, to_device(seq, DEV), to_device(pos, DEV), **SP)
+    torch.cuda.synchronize()
+    d = dg.cpu().numpy()
+    pick = np.sort(np.random.default_rng(0).choice(S, nsample, replace=False))
+    dref, _ = oracle.draft_sample(q[pick], seq[pick], pos[pick], SP["temperature"], SP["top_k"],
+                                  SP["top_p"], SP["seed"], "bf16")
+    tie_free = np.array_equal(dref, d[pick])
+    d[pick] = dref                      # oracle drafts on the compared sequences
+    ref = oracle.verify_block(p[pick], q[pick], dref, seq[pick], pos[pick], SP["temperature"],
+                              SP["top_k"], SP["top_p"], SP["seed"], "bf16")
+    r = uno.uno_verify_block(pd, qd, to_device(d.astype(np.int32), DEV), to_device(seq, DEV),
+                             to_device(pos, DEV), **SP)
+    torch.cuda.synchronize()
+    gpu = {k: v.cpu().numpy() for k, v in r.items()}
+    st = compare_verify(gpu, ref, b, seqs=pick)
+    flags = gpu["diag"][..., 3].astype(np.int64)
+    print(name, st, "draft sampler exact on sample:", tie_free, "mean accept_len",
+          gpu["accept_len"].mean(), "overflow slots", int(np.sum(flags & 64 != 0)),
+          "near-tie slots", int(np.sum(flags & oracle.TIE_MASK != 0)))
+    assert st["exact"] >= nsample - 1
+    assert not np.any(flags & 64)
+    assert np.all((gpu["accept_len"] >= 1) & (gpu["accept_len"] <= b))
+
+
+def test_repeat_runs_are_identical():
+    uno = _uno()
+    p, q = workloads.verify_logits(dict(workloads.VERIFY_CONFIGS["qwen"], S=16, b=16), V=151936)
+    S = 16
+    seq, pos = to_device(np.arange(S, dtype=np.int64), DEV), to_device(np.zeros(S, dtype=np.int64), DEV)
+    pd, qd = to_device(p, DEV), to_device(q, DEV)
+    d, _ = uno.uno_draft_sample(qd, seq, pos, **SP)
+    first = None
+    for _ in range(20):
+        r = uno.uno_verify_block(pd, qd, d, seq, pos, **SP)
+        cur = torch.cat([r["out_tokens"].flatten(), r["accept_len"], r["resampled"]]).cpu()
+        if first is None:
+            first = cur
+        assert torch.equal(cur, first)
