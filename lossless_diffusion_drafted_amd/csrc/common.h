@@ -41,6 +41,19 @@ __device__ __forceinline__ uint4 load_nt16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Raw buffer loads: a range-checked view of one row. Reads past num_records
+// return zero instead of faulting, so every lane issues exactly one load per chunk
+// and the compiler can count outstanding loads across a pipelined loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_row_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);   // gfx9-family dword3
+}
+// voff: per-lane byte offset; soff: wave-uniform byte offset (kept in an SGPR).
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---------------------------------------------------------------------------
 // Wave64 reductions and scans (lane shuffles; every lane gets the result).
 template <typename T>

@@ -81,7 +81,7 @@ struct FilterParams {
 };
 
 // --- block-wide reductions (all 256 threads call; result broadcast) ---------
-__device__ double block_sum_d(double v, Shared& sh) {
+__device__ __forceinline__ double block_sum_d(double v, Shared& sh) {
   v = wave_sum(v);
   __syncthreads();
   if ((threadIdx.x & (kWave - 1)) == 0) sh.red_d[threadIdx.x / kWave] = v;
@@ -91,7 +91,7 @@ __device__ double block_sum_d(double v, Shared& sh) {
   for (int i = 0; i < VW; ++i) t += sh.red_d[i];
   return t;
 }
-__device__ float block_min_f(float v, Shared& sh) {
+__device__ __forceinline__ float block_min_f(float v, Shared& sh) {
   v = wave_min(v);
   __syncthreads();
   if ((threadIdx.x & (kWave - 1)) == 0) sh.red_f[threadIdx.x / kWave] = v;
@@ -101,7 +101,7 @@ __device__ float block_min_f(float v, Shared& sh) {
   for (int i = 1; i < VW; ++i) t = fminf(t, sh.red_f[i]);
   return t;
 }
-__device__ unsigned block_max_u(unsigned v, Shared& sh) {
+__device__ __forceinline__ unsigned block_max_u(unsigned v, Shared& sh) {
   v = wave_max(v);
   __syncthreads();
   if ((threadIdx.x & (kWave - 1)) == 0) sh.red_u[threadIdx.x / kWave] = v;
@@ -111,7 +111,7 @@ __device__ unsigned block_max_u(unsigned v, Shared& sh) {
   for (int i = 1; i < VW; ++i) t = max(t, sh.red_u[i]);
   return t;
 }
-__device__ unsigned block_min_u(unsigned v, Shared& sh) {
+__device__ __forceinline__ unsigned block_min_u(unsigned v, Shared& sh) {
   v = wave_min(v);
   __syncthreads();
   if ((threadIdx.x & (kWave - 1)) == 0) sh.red_u[threadIdx.x / kWave] = v;
@@ -121,7 +121,7 @@ __device__ unsigned block_min_u(unsigned v, Shared& sh) {
   for (int i = 1; i < VW; ++i) t = min(t, sh.red_u[i]);
   return t;
 }
-__device__ unsigned block_or_u(unsigned v, Shared& sh) {
+__device__ __forceinline__ unsigned block_or_u(unsigned v, Shared& sh) {
   v = wave_or(v);
   __syncthreads();
   if ((threadIdx.x & (kWave - 1)) == 0) sh.red_u[threadIdx.x / kWave] = v;
@@ -131,7 +131,7 @@ __device__ unsigned block_or_u(unsigned v, Shared& sh) {
   for (int i = 0; i < VW; ++i) t |= sh.red_u[i];
   return t;
 }
-__device__ int block_max_i(int v, Shared& sh) {
+__device__ __forceinline__ int block_max_i(int v, Shared& sh) {
   v = wave_max(v);
   __syncthreads();
   if ((threadIdx.x & (kWave - 1)) == 0) sh.red_i[threadIdx.x / kWave] = v;
@@ -141,7 +141,7 @@ __device__ int block_max_i(int v, Shared& sh) {
   for (int i = 1; i < VW; ++i) t = max(t, sh.red_i[i]);
   return t;
 }
-__device__ int block_min_i(int v, Shared& sh) {
+__device__ __forceinline__ int block_min_i(int v, Shared& sh) {
   v = wave_min(v);
   __syncthreads();
   if ((threadIdx.x & (kWave - 1)) == 0) sh.red_i[threadIdx.x / kWave] = v;
@@ -190,7 +190,7 @@ template <> struct Elem<float> {
 
 // --- one row: stream, candidates, exact tie-inclusive top-k, fp64 filter -------
 template <typename E, bool VEC>
-__device__ int filter_row(const E* __restrict__ row, int V, const FilterParams& fp,
+__device__ __forceinline__ int filter_row(const E* __restrict__ row, int V, const FilterParams& fp,
                           Shared& sh, Dist& out, double& topp_gap) {
   using EL = Elem<E>;
   constexpr int VN = EL::VN;
@@ -201,30 +201,45 @@ __device__ int filter_row(const E* __restrict__ row, int V, const FilterParams& 
   const int ntiles = (nchunks + PER_TILE - 1) / PER_TILE;
   topp_gap = INFINITY;
 
+  // Vector path: one range-checked buffer load per chunk (bytes past the row read
+  // as zero and are masked to -inf by index in the last tile). Scalar path for
+  // rows that are not 16-byte aligned.
+  const int full_tiles = VEC ? nfull / PER_TILE : 0;
+  const __amdgpu_buffer_rsrc_t rsrc = make_row_rsrc(row, uint32_t(V) * uint32_t(sizeof(E)));
   auto load_tile = [&](uint4 (&r)[UNR], int t) {
+    if (VEC) {
+      const uint32_t voff = uint32_t(tid) * 16u;
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int c = t * PER_TILE + u * VT + tid;
-      if (VEC && c < nfull) {
-        r[u] = load_nt16(reinterpret_cast<const uint4*>(row) + c);
-      } else if (c < nchunks) {
-        r[u] = EL::load_partial(row, c * VN, V);
-      } else {
-        r[u] = VN == 8 ? make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u)
-                       : make_uint4(0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u);
+      for (int u = 0; u < UNR; ++u)
+        r[u] = buffer_load16(rsrc, voff, uint32_t(t * PER_TILE + u * VT) * 16u);
+    } else {
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int c = t * PER_TILE + u * VT + tid;
+        if (c < nchunks) {
+          r[u] = EL::load_partial(row, c * VN, V);
+        } else {
+          r[u] = VN == 8 ? make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u)
+                         : make_uint4(0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u);
+        }
       }
     }
   };
   auto process_tile = [&](const uint4 (&r)[UNR], int t, float thr) {
+    const bool tail = t >= full_tiles;
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       float x[VN];
       EL::unpack(r[u], x);
+      const int e0 = (t * PER_TILE + u * VT + tid) * VN;
+      if (tail) {
+#pragma unroll
+        for (int j = 0; j < VN; ++j) x[j] = (e0 + j < V) ? x[j] : -INFINITY;
+      }
       float mx = x[0];
 #pragma unroll
       for (int j = 1; j < VN; ++j) mx = fmaxf(mx, x[j]);
       if (mx >= thr) {
-        const int e0 = (t * PER_TILE + u * VT + tid) * VN;
 #pragma unroll
         for (int j = 0; j < VN; ++j) {
           if (x[j] >= thr && e0 + j < V) {
@@ -238,8 +253,11 @@ __device__ int filter_row(const E* __restrict__ row, int V, const FilterParams& 
 
   if (tid == 0) sh.cnt = 0;
   uint4 A[UNR], B[UNR];
+  // Both buffers are always loaded (tiles past the row read as zero on the vector
+  // path), so the number of loads in flight is the same on every path and each
+  // wait covers exactly the tile about to be processed.
   load_tile(A, 0);
-  if (ntiles > 1) load_tile(B, 1);
+  if (VEC || ntiles > 1) load_tile(B, 1);
 
   // Lower bound of the k-th largest value from the first tile's lane maxima.
   float thr = -INFINITY;
@@ -249,8 +267,9 @@ __device__ int filter_row(const E* __restrict__ row, int V, const FilterParams& 
     for (int u = 0; u < UNR; ++u) {
       float x[VN];
       EL::unpack(A[u], x);
+      const int e0 = (u * VT + tid) * VN;
 #pragma unroll
-      for (int j = 0; j < VN; ++j) m = fmaxf(m, x[j]);
+      for (int j = 0; j < VN; ++j) m = (e0 + j < V) ? fmaxf(m, x[j]) : m;
     }
     const int c = (fp.k_eff + VW - 1) / VW;     // <= 64
     int cnt_ge = 0;
@@ -269,13 +288,22 @@ __device__ int filter_row(const E* __restrict__ row, int V, const FilterParams& 
     __syncthreads();
   }
 
-  process_tile(A, 0, thr);
-  for (int t = 1; t < ntiles; t += 2) {
-    if (t + 1 < ntiles) load_tile(A, t + 1);
-    process_tile(B, t, thr);
-    if (t + 1 < ntiles) {
-      if (t + 2 < ntiles) load_tile(B, t + 2);
-      process_tile(A, t + 1, thr);
+  if (VEC) {
+    for (int t = 0; t < ntiles; t += 2) {
+      process_tile(A, t, thr);
+      load_tile(A, t + 2);
+      if (t + 1 < ntiles) process_tile(B, t + 1, thr);
+      load_tile(B, t + 3);
+    }
+  } else {
+    process_tile(A, 0, thr);
+    for (int t = 1; t < ntiles; t += 2) {
+      if (t + 1 < ntiles) load_tile(A, t + 1);
+      process_tile(B, t, thr);
+      if (t + 1 < ntiles) {
+        if (t + 2 < ntiles) load_tile(B, t + 2);
+        process_tile(A, t + 1, thr);
+      }
     }
   }
   __syncthreads();
@@ -428,7 +456,7 @@ __device__ int filter_row(const E* __restrict__ row, int V, const FilterParams& 
 // j with u*Z < C_j, where C is the inclusive prefix sum and Z = C_{n-1}; falls
 // back to the last positive weight. Sets *tie when u*Z lies within 1e-6*Z of a
 // decision boundary.
-__device__ int block_icdf(double w, int n, double u, Shared& sh, bool* tie) {
+__device__ __forceinline__ int block_icdf(double w, int n, double u, Shared& sh, bool* tie) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const double v = tid < n ? w : 0.0;
   const double inc = wave_inclusive_scan(v);
@@ -461,7 +489,7 @@ __device__ int block_icdf(double w, int n, double u, Shared& sh, bool* tie) {
   return jj;
 }
 
-__device__ double lookup_prob(const Dist& d, int tok) {
+__device__ __forceinline__ double lookup_prob(const Dist& d, int tok) {
   int lo = 0, hi = d.n;                 // binary search over ascending ids
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
@@ -470,7 +498,7 @@ __device__ double lookup_prob(const Dist& d, int tok) {
   return (lo < d.n && d.ids[lo] == tok) ? d.prob[lo] : 0.0;
 }
 
-__device__ FilterParams make_filter_params(const SamplingArgs& sp, int V) {
+__device__ __forceinline__ FilterParams make_filter_params(const SamplingArgs& sp, int V) {
   FilterParams fp;
   fp.T = sp.temperature;
   fp.greedy = !(sp.temperature > 0.0);
