@@ -157,14 +157,45 @@ int uno_draft_sample(const void* q_logits, int dtype, const int64_t* seq_ids,
 }
 
 size_t uno_tv_loss_workspace(int R, int V) {
-  (void)R;
   (void)V;
-  return 256;
+  return uno::tv_workspace_bytes(R);
 }
 
-int uno_tv_loss_fwd_bwd(const void*, const void*, int, const uint8_t*, int, int, float, float*,
-                        float*, void*, void*, size_t, void*) {
-  return fail(UNO_ERR_UNSUPPORTED, "uno_tv_loss_fwd_bwd: not built yet");
+int uno_tv_loss_fwd_bwd(const void* teacher_logits, const void* student_logits, int dtype,
+                        const uint8_t* response_mask, int R, int V, float temperature,
+                        float* loss, float* tv_rows, void* grad_student,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "uno_tv_loss_fwd_bwd";
+  if (R < 0) return fail(UNO_ERR_INVALID_ARG, "%s: R = %d < 0", fn, R);
+  if (V < 1) return fail(UNO_ERR_INVALID_ARG, "%s: vocabulary V = %d < 1", fn, V);
+  if (!(temperature > 0.0f) || isinf(temperature))
+    return fail(UNO_ERR_INVALID_ARG, "%s: temperature must be finite and > 0 (got %g)", fn, double(temperature));
+  if (dtype != UNO_DTYPE_F32 && dtype != UNO_DTYPE_BF16)
+    return fail(UNO_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+  if (!loss) return fail(UNO_ERR_INVALID_ARG, "%s: loss is null", fn);
+  if (R > 0 && (!teacher_logits || !student_logits || !response_mask))
+    return fail(UNO_ERR_INVALID_ARG, "%s: a required pointer is null", fn);
+  const size_t need = uno_tv_loss_workspace(R, V);
+  if (!workspace || ws_bytes < need)
+    return fail(UNO_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, need);
+  const int vmax = uno::tv_max_vocab(dtype == UNO_DTYPE_BF16);
+  if (vmax <= 0) return fail(UNO_ERR_HIP, "%s: occupancy query failed", fn);
+  if (V > vmax)
+    return fail(UNO_ERR_UNSUPPORTED, "%s: V = %d exceeds the %d logits one row team holds on this device",
+                fn, V, vmax);
+  uno::TvArgs a;
+  a.teacher = teacher_logits;
+  a.student = student_logits;
+  a.bf16 = dtype == UNO_DTYPE_BF16;
+  a.mask = response_mask;
+  a.R = R;
+  a.V = V;
+  a.temperature = temperature;
+  a.loss = loss;
+  a.tv_rows = tv_rows;
+  a.grad = grad_student;
+  a.ws = workspace;
+  return hip_status(uno::launch_tv(a, static_cast<hipStream_t>(stream)), "uno_tv_loss_fwd_bwd launch");
 }
 
 size_t uno_gated_lora_linear_workspace(int M, int N, int K, int r) {

@@ -42,6 +42,19 @@ struct DraftArgs {
   int32_t* flags;
 };
 
+struct TvArgs {
+  const void* teacher;
+  const void* student;
+  bool bf16;
+  const uint8_t* mask;
+  int R, V;
+  float temperature;
+  float* loss;
+  float* tv_rows;
+  void* grad;
+  void* ws;
+};
+
 // Largest top-k the single-pass selection handles, and largest vocabulary that
 // may be taken whole when top-k is off.
 constexpr int kVerifyKMaxFast = 256;
@@ -50,6 +63,9 @@ constexpr int kVerifyCandCap = 2048;
 size_t verify_workspace_bytes(int S, int b);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_draft(const DraftArgs& a, hipStream_t stream);
+size_t tv_workspace_bytes(int R);
+int tv_max_vocab(bool bf16);          // largest V one row team covers on this device
+hipError_t launch_tv(const TvArgs& a, hipStream_t stream);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t stream);
 
 }  // namespace uno

@@ -1,0 +1,527 @@
+// Total-variation self-distillation loss with its student gradient, fused into
+// one pass over the logits ("LoopUno: Turning Agentic Looped LLMs into
+// Diffusion LLMs in One Hour", "How it works" -> "Training is self-distillation":
+// the student is pushed towards the frozen teacher by minimising TV on the
+// response tokens, and 1 - TV is the acceptance rate of lossless verification).
+//
+// Per response row r (p = softmax(teacher/T), q = softmax(student/T), full vocab):
+//   TV_r = 1/2 sum_v |p_v - q_v|,   G_r = 1/2 sum_v q_v sign(q_v - p_v),
+//   grad[r, j] = q_j (1/2 sign(q_j - p_j) - G_r) / (T N),   N = #response rows,
+//   loss = sum_r TV_r / N.
+// Rows outside the response mask get TV 0 and a zero gradient.
+//
+// Design (HBM-bound: read both rows once, write the gradient once).
+// * A row is split over a team of G workgroups that stay resident for the whole
+//   launch (cooperative launch). Each thread keeps its slice of both rows in
+//   registers as fp32 exp values, so nothing is read twice: per element the
+//   three passes cost about 25 VALU lane-ops, with 6 of them for exponentials.
+// * Pass 1: per-thread max and sum of exp2((x - m) log2(e)/T); workgroup
+//   partials go to the team through device-coherent records, then a team
+//   barrier. Pass 2: p, q from the stored exps, sum |q - p| and sum q sign(q - p);
+//   the registers now hold (sign, q). Second barrier. Pass 3: the gradient,
+//   rounded to bf16 by the hardware conversion, written with streaming stores.
+// * Team barriers are counters in the workspace with bounded spins; a spin that
+//   runs out sets an abort flag that every waiter polls, so every wait ends (the
+//   loss is then NaN).
+
+#include "../../include/uno.h"
+#include "common.h"
+#include "kernels.h"
+
+#include <mutex>
+
+namespace uno {
+namespace {
+
+constexpr int TT = 512;                 // threads per workgroup
+constexpr int TWAVES = TT / kWave;
+constexpr int EPT = 40;                 // elements of each row per thread
+constexpr int CHUNK = TT * EPT;         // elements of each row per workgroup
+constexpr int kMaxWg = 4096;            // resident workgroups the workspace can serve
+constexpr unsigned kSpinLimit = 1u << 21;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct TvPlan {
+  int G;          // workgroups per row team
+  int nteams;
+  int xcd;        // 1: team members share an XCD (grid is a multiple of 8 G)
+};
+
+// Workspace: [header | team counters (64 B each) | team records (64 B per
+// workgroup) | per-row TV (double)].
+struct TvHeader {
+  unsigned done;
+  unsigned abort;
+  unsigned nresp;
+};
+constexpr size_t kCtrOff = 256;
+constexpr size_t kRecOff = kCtrOff + size_t(kMaxWg) * 64;
+constexpr size_t kRowOff = kRecOff + size_t(kMaxWg) * 64;
+
+struct TvLds {
+  float wred[TWAVES][4];
+  double rec[64][4];
+  float norm[4];
+  int ok;
+  int last;
+};
+
+template <typename E> struct TvElem;
+template <> struct TvElem<uint16_t> {
+  static constexpr int VN = 8;
+  __device__ static void unpack(const uint4& v, float (&x)[8]) {
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+  }
+  __device__ static float scalar(const uint16_t* p) { return bf16_to_f32(*p); }
+  __device__ static uint4 pack(const float (&g)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t lo = __builtin_bit_cast(uint16_t, (__bf16)g[2 * i]);
+      const uint16_t hi = __builtin_bit_cast(uint16_t, (__bf16)g[2 * i + 1]);
+      w[i] = uint32_t(lo) | (uint32_t(hi) << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  __device__ static void store_scalar(uint16_t* p, float g) { *p = __builtin_bit_cast(uint16_t, (__bf16)g); }
+};
+template <> struct TvElem<float> {
+  static constexpr int VN = 4;
+  __device__ static void unpack(const uint4& v, float (&x)[4]) {
+    x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
+  }
+  __device__ static float scalar(const float* p) { return *p; }
+  __device__ static uint4 pack(const float (&g)[4]) {
+    return make_uint4(__float_as_uint(g[0]), __float_as_uint(g[1]), __float_as_uint(g[2]),
+                      __float_as_uint(g[3]));
+  }
+  __device__ static void store_scalar(float* p, float g) { *p = g; }
+};
+
+// Element j of this thread's slice sits at row offset c0 + (j / VN * TT + tid) * VN + j % VN.
+// The buffer view starts at the slice (the range check covers only the per-lane
+// offset), so lanes past the row end read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const void* row, int V, int c0, int esize) {
+  return make_row_rsrc(static_cast<const char*>(row) + size_t(c0) * esize, uint32_t(size_t(V - c0) * esize));
+}
+
+template <typename E>
+__device__ __forceinline__ void issue_slice(const E* row, int V, int c0, uint4 (&raw)[EPT / TvElem<E>::VN]) {
+  const __amdgpu_buffer_rsrc_t rs = slice_rsrc(row, V, c0, int(sizeof(E)));
+#pragma unroll
+  for (int u = 0; u < EPT / TvElem<E>::VN; ++u)
+    raw[u] = buffer_load16(rs, uint32_t((u * TT + int(threadIdx.x)) * 16), 0u);
+}
+
+template <typename E>
+__device__ __forceinline__ void unpack_slice(const uint4 (&raw)[EPT / TvElem<E>::VN], float (&x)[EPT]) {
+  constexpr int VN = TvElem<E>::VN;
+#pragma unroll
+  for (int u = 0; u < EPT / VN; ++u) {
+    float v[VN];
+    TvElem<E>::unpack(raw[u], v);
+#pragma unroll
+    for (int j = 0; j < VN; ++j) x[u * VN + j] = v[j];
+  }
+}
+
+// Rows that are not 16-byte aligned: element loads (correct, not fast).
+template <typename E>
+__device__ __forceinline__ void load_slice_scalar(const E* row, int V, int c0, float (&x)[EPT]) {
+  constexpr int VN = TvElem<E>::VN;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < EPT / VN; ++u) {
+#pragma unroll
+    for (int j = 0; j < VN; ++j) {
+      const int e = c0 + (u * TT + tid) * VN + j;
+      x[u * VN + j] = e < V ? TvElem<E>::scalar(row + e) : 0.0f;
+    }
+  }
+}
+
+// Both slices of a row; on the vector path every load is issued before any is
+// waited on.
+template <typename E, bool VEC>
+__device__ __forceinline__ void load_slices(const E* trow, const E* srow, int V, int c0, float (&xt)[EPT],
+                                            float (&xs)[EPT]) {
+  if constexpr (VEC) {
+    uint4 rt[EPT / TvElem<E>::VN], rs[EPT / TvElem<E>::VN];
+    issue_slice<E>(trow, V, c0, rt);
+    issue_slice<E>(srow, V, c0, rs);
+    unpack_slice<E>(rt, xt);
+    unpack_slice<E>(rs, xs);
+  } else {
+    load_slice_scalar<E>(trow, V, c0, xt);
+    load_slice_scalar<E>(srow, V, c0, xs);
+  }
+}
+
+// Gradient of this thread's slice from the stored (sign, q): g = q (s h + g0),
+// computed and written one 16-byte vector at a time. With zero = true the slice
+// is cleared instead (rows outside the response mask).
+template <typename E, bool VEC>
+__device__ __forceinline__ void store_grad(E* row, int V, int c0, const float (&sg)[EPT], const float (&q)[EPT],
+                                           float h, float g0, bool zero) {
+  using EL = TvElem<E>;
+  constexpr int VN = EL::VN;
+  const int tid = threadIdx.x;
+  if constexpr (VEC) {
+    const __amdgpu_buffer_rsrc_t rs = slice_rsrc(row, V, c0, int(sizeof(E)));
+#pragma unroll
+    for (int u = 0; u < EPT / VN; ++u) {
+      float v[VN];
+#pragma unroll
+      for (int j = 0; j < VN; ++j) v[j] = zero ? 0.0f : q[u * VN + j] * fmaf(sg[u * VN + j], h, g0);
+      const uint4 w = EL::pack(v);
+      const u32x4_t wv = {w.x, w.y, w.z, w.w};
+      // Out-of-range stores are dropped by the buffer range check.
+      __builtin_amdgcn_raw_buffer_store_b128(wv, rs, uint32_t((u * TT + tid) * 16), 0u, kBufNonTemporal);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < EPT / VN; ++u) {
+#pragma unroll
+      for (int j = 0; j < VN; ++j) {
+        const int e = c0 + (u * TT + tid) * VN + j;
+        const float g = zero ? 0.0f : q[u * VN + j] * fmaf(sg[u * VN + j], h, g0);
+        if (e < V) EL::store_scalar(row + e, g);
+      }
+    }
+  }
+}
+
+// Team barrier: thread 0 has published this workgroup's record; count the
+// arrival and wait until all G members of barrier number `n` have arrived.
+__device__ bool team_barrier(unsigned* ctr, unsigned target, unsigned* abort_flag, TvLds& sh) {
+  if (threadIdx.x == 0) {
+    // The record was written with device-coherent stores; the wait retires them
+    // before the arrival is counted.
+    __builtin_amdgcn_s_waitcnt(0);
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool ok = true;
+    unsigned spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if ((++spins & 63u) == 0u) {
+        if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) { ok = false; break; }
+        if (spins > kSpinLimit) {
+          __hip_atomic_store(abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = false;
+          break;
+        }
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    sh.ok = ok ? 1 : 0;
+  }
+  __syncthreads();
+  return sh.ok != 0;
+}
+
+__device__ __forceinline__ void put_record(double* rec, double a, double b, double c, double d) {
+  __hip_atomic_store(&rec[0], a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&rec[1], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&rec[2], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&rec[3], d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The G records of the team (4 doubles each) into LDS.
+__device__ __forceinline__ void get_records(const double* team_rec, int G, int slot, TvLds& sh) {
+  const int tid = threadIdx.x;
+  if (tid < 4 * G) {
+    const int j = tid >> 2, k = tid & 3;
+    sh.rec[j][k] = __hip_atomic_load(&team_rec[j * 8 + slot * 4 + k], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+}
+
+template <typename E, bool VEC>
+__global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(4, 4))) void tv_kernel(TvArgs a, TvPlan pl) {
+  __shared__ TvLds sh;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int G = pl.G;
+  int team, member;
+  if (pl.xcd) {
+    const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+    team = x * (pl.nteams >> 3) + i / G;
+    member = i % G;
+  } else {
+    team = blockIdx.x / G;
+    member = blockIdx.x % G;
+  }
+  char* ws = static_cast<char*>(a.ws);
+  TvHeader* hdr = reinterpret_cast<TvHeader*>(ws);
+  unsigned* ctr = reinterpret_cast<unsigned*>(ws + kCtrOff + size_t(team) * 64);
+  double* team_rec = reinterpret_cast<double*>(ws + kRecOff + size_t(team) * G * 64);
+  double* my_rec = team_rec + member * 8;
+  double* row_tv = reinterpret_cast<double*>(ws + kRowOff);
+
+  const int V = a.V;
+  const int c0 = member * CHUNK;
+  const float c = float(double(kLog2e) / double(a.temperature));
+  const unsigned nresp = hdr->nresp;
+  const float inv_tn = nresp ? float(1.0 / (double(a.temperature) * double(nresp))) : 0.0f;
+  const E* tbase = static_cast<const E*>(a.teacher);
+  const E* sbase = static_cast<const E*>(a.student);
+  E* gbase = static_cast<E*>(a.grad);
+  unsigned nbar = 0;
+  bool ok = true;
+
+  for (int r = team; ok && r < a.R; r += pl.nteams) {
+    E* grow = gbase ? gbase + size_t(r) * V : nullptr;
+    if (a.mask[r] == 0) {
+      if (grow) {
+        float z[EPT];
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) z[j] = 0.0f;
+        store_grad<E, VEC>(grow, V, c0, z, z, 0.0f, 0.0f, true);
+      }
+      if (member == 0 && tid == 0 && a.tv_rows) a.tv_rows[r] = 0.0f;
+      continue;
+    }
+    float et[EPT], es[EPT];
+    load_slices<E, VEC>(tbase + size_t(r) * V, sbase + size_t(r) * V, V, c0, et, es);
+    if (c0 + CHUNK > V) {                       // last slice of the row: mask the tail
+      constexpr int VN = TvElem<E>::VN;
+      const int lim = V - c0 - tid * VN;        // element j is in the row iff (j/VN)*TT*VN + j%VN < lim
+      if constexpr (VEC) {
+        // V is a multiple of VN here: each 16-byte vector is wholly in or out.
+#pragma unroll
+        for (int u = 0; u < EPT / VN; ++u) {
+          if (u * TT * VN >= lim) {
+#pragma unroll
+            for (int j = 0; j < VN; ++j) { et[u * VN + j] = -INFINITY; es[u * VN + j] = -INFINITY; }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+          if ((j / VN) * TT * VN + (j % VN) >= lim) { et[j] = -INFINITY; es[j] = -INFINITY; }
+        }
+      }
+    }
+    // ---- pass 1: thread max, exps relative to it, thread sums ----
+    float mt = -INFINITY, ms = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) { mt = fmaxf(mt, et[j]); ms = fmaxf(ms, es[j]); }
+    if (mt == -INFINITY) mt = 0.0f;             // thread holds no element of the row
+    if (ms == -INFINITY) ms = 0.0f;
+    const float bt = -mt * c, bs = -ms * c;
+    float zt = 0.0f, zs = 0.0f;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      et[j] = __builtin_amdgcn_exp2f(fmaf(et[j], c, bt));
+      es[j] = __builtin_amdgcn_exp2f(fmaf(es[j], c, bs));
+      zt += et[j];
+      zs += es[j];
+    }
+    // Wave partials, then workgroup partial by thread 0 (fp64), then the team.
+    {
+      const float wmt = wave_max(zt > 0.0f ? mt : -INFINITY);
+      const float wms = wave_max(zs > 0.0f ? ms : -INFINITY);
+      const float st = zt > 0.0f ? zt * __builtin_amdgcn_exp2f((mt - wmt) * c) : 0.0f;
+      const float ss = zs > 0.0f ? zs * __builtin_amdgcn_exp2f((ms - wms) * c) : 0.0f;
+      const float wzt = wave_sum(st), wzs = wave_sum(ss);
+      if (lane == 0) { sh.wred[wid][0] = wmt; sh.wred[wid][1] = wzt; sh.wred[wid][2] = wms; sh.wred[wid][3] = wzs; }
+      __syncthreads();
+      if (tid == 0) {
+        float Mt = -INFINITY, Ms = -INFINITY;
+        double Zt = 0.0, Zs = 0.0;
+        for (int w = 0; w < TWAVES; ++w) { Mt = fmaxf(Mt, sh.wred[w][0]); Ms = fmaxf(Ms, sh.wred[w][2]); }
+        for (int w = 0; w < TWAVES; ++w) {
+          if (sh.wred[w][1] > 0.0f) Zt += double(sh.wred[w][1] * __builtin_amdgcn_exp2f((sh.wred[w][0] - Mt) * c));
+          if (sh.wred[w][3] > 0.0f) Zs += double(sh.wred[w][3] * __builtin_amdgcn_exp2f((sh.wred[w][2] - Ms) * c));
+        }
+        put_record(my_rec, double(Mt), Zt, double(Ms), Zs);
+      }
+    }
+    ++nbar;
+    if (!team_barrier(ctr, nbar * unsigned(G), &hdr->abort, sh)) { ok = false; break; }
+    get_records(team_rec, G, 0, sh);
+    if (tid == 0) {
+      float Mt = -INFINITY, Ms = -INFINITY;
+      double Zt = 0.0, Zs = 0.0;
+      for (int j = 0; j < G; ++j) { Mt = fmaxf(Mt, float(sh.rec[j][0])); Ms = fmaxf(Ms, float(sh.rec[j][2])); }
+      for (int j = 0; j < G; ++j) {
+        if (sh.rec[j][1] > 0.0) Zt += sh.rec[j][1] * double(__builtin_amdgcn_exp2f((float(sh.rec[j][0]) - Mt) * c));
+        if (sh.rec[j][3] > 0.0) Zs += sh.rec[j][3] * double(__builtin_amdgcn_exp2f((float(sh.rec[j][2]) - Ms) * c));
+      }
+      sh.norm[0] = Mt;
+      sh.norm[1] = float(log2(Zt));
+      sh.norm[2] = Ms;
+      sh.norm[3] = float(log2(Zs));
+    }
+    __syncthreads();
+    // p = et * at, q = es * as: exp2 of the thread-max offset minus log2 Z.
+    const float at = __builtin_amdgcn_exp2f((mt - sh.norm[0]) * c - sh.norm[1]);
+    const float as = __builtin_amdgcn_exp2f((ms - sh.norm[2]) * c - sh.norm[3]);
+    // ---- pass 2: |q - p| and q sign(q - p); keep (sign, q) ----
+    float tvs = 0.0f, gs = 0.0f;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      // Rounded products, not contracted into the subtraction, so that equal
+      // rows give d == 0 exactly.
+#pragma clang fp contract(off)
+      const float p = et[j] * at, q = es[j] * as;
+      const float d = q - p;
+      // sign(d): +-1 for |d| >= 2^-126, 0 for d == 0
+      const float s = __builtin_amdgcn_fmed3f(d * 0x1p126f, -1.0f, 1.0f);
+      tvs = fmaf(d, s, tvs);
+      gs = fmaf(q, s, gs);
+      et[j] = s;
+      es[j] = q;
+    }
+    __syncthreads();                           // sh.rec / sh.wred reuse
+    {
+      const float wt = wave_sum(tvs), wg = wave_sum(gs);
+      if (lane == 0) { sh.wred[wid][0] = wt; sh.wred[wid][1] = wg; }
+      __syncthreads();
+      if (tid == 0) {
+        double T = 0.0, Gs = 0.0;
+        for (int w = 0; w < TWAVES; ++w) { T += double(sh.wred[w][0]); Gs += double(sh.wred[w][1]); }
+        __hip_atomic_store(&my_rec[4], T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&my_rec[5], Gs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    ++nbar;
+    if (!team_barrier(ctr, nbar * unsigned(G), &hdr->abort, sh)) { ok = false; break; }
+    get_records(team_rec, G, 1, sh);
+    double tv = 0.0, gsum = 0.0;
+    for (int j = 0; j < G; ++j) { tv += sh.rec[j][0]; gsum += sh.rec[j][1]; }
+    tv *= 0.5;
+    gsum *= 0.5;
+    if (member == 0 && tid == 0) {
+      if (a.tv_rows) a.tv_rows[r] = float(tv);
+      __hip_atomic_store(&row_tv[r], tv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // ---- pass 3: gradient ----
+    if (grow) {
+      const float h = 0.5f * inv_tn, g0 = float(-gsum * double(inv_tn));
+      store_grad<E, VEC>(grow, V, c0, et, es, h, g0, false);
+    }
+    __syncthreads();                           // sh.rec reuse by the next row
+  }
+
+  // ---- completion: the last workgroup reduces the loss in a fixed order ----
+  if (tid == 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    const unsigned old = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.last = old == gridDim.x - 1 ? 1 : 0;
+  }
+  __syncthreads();
+  if (!sh.last) return;
+  double acc = 0.0;
+  for (int r = tid; r < a.R; r += TT)
+    if (a.mask[r]) acc += __hip_atomic_load(&row_tv[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  acc = wave_sum(acc);
+  __shared__ double wsum[TWAVES];
+  if (lane == 0) wsum[wid] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    double tot = 0.0;
+    for (int w = 0; w < TWAVES; ++w) tot += wsum[w];
+    const bool aborted = __hip_atomic_load(&hdr->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+    *a.loss = aborted ? __builtin_nanf("") : (nresp ? float(tot / double(nresp)) : 0.0f);
+    __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&hdr->abort, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  for (int t = tid; t < pl.nteams; t += TT)
+    __hip_atomic_store(reinterpret_cast<unsigned*>(ws + kCtrOff + size_t(t) * 64), 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Counts the response rows and sets the loss to 0 (the main kernel overwrites it
+// when there is at least one response row).
+__global__ __launch_bounds__(1024) void tv_count_kernel(const uint8_t* mask, int R, void* ws, float* loss) {
+  unsigned n = 0;
+  for (int r = threadIdx.x; r < R; r += 1024) n += mask[r] != 0;
+  n = wave_sum(n);
+  __shared__ unsigned part[1024 / kWave];
+  if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned t = 0;
+    for (int w = 0; w < 1024 / kWave; ++w) t += part[w];
+    static_cast<TvHeader*>(ws)->nresp = t;
+    *loss = 0.0f;
+  }
+}
+
+template <typename E, bool VEC>
+const void* tv_kernel_ptr() {
+  return reinterpret_cast<const void*>(&tv_kernel<E, VEC>);
+}
+
+// Resident workgroups of one instantiation on the current device (cached).
+int resident_wgs(const void* fn, int slot) {
+  static std::mutex mu;
+  static int cache[64][4];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cache[dev][slot] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, TT, 0) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    const int n = per_cu * cus;
+    cache[dev][slot] = n < kMaxWg ? n : kMaxWg;
+  }
+  return cache[dev][slot];
+}
+
+template <typename E, bool VEC>
+hipError_t launch_tv_t(const TvArgs& a, int slot, hipStream_t stream) {
+  const void* fn = tv_kernel_ptr<E, VEC>();
+  const int res = resident_wgs(fn, slot);
+  const int G = (a.V + CHUNK - 1) / CHUNK;
+  if (res <= 0) return hipErrorInvalidDevice;
+  if (G > res || G > 64) return hipErrorInvalidConfiguration;
+  TvPlan pl;
+  pl.G = G;
+  int nteams = res / G;
+  if (nteams > a.R) nteams = a.R;
+  pl.xcd = 0;
+  if (nteams >= 8) {
+    nteams &= ~7;
+    pl.xcd = 1;
+  }
+  pl.nteams = nteams;
+  TvArgs args = a;
+  void* params[] = {&args, &pl};
+  return hipLaunchCooperativeKernel(fn, dim3(nteams * G), dim3(TT), params, 0, stream);
+}
+
+template <typename E>
+bool tv_rows_aligned(const void* p, int V) {
+  return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && ((size_t(V) * sizeof(E)) % 16 == 0);
+}
+
+}  // namespace
+
+size_t tv_workspace_bytes(int R) { return kRowOff + size_t(R > 0 ? R : 0) * 8; }
+
+int tv_max_vocab(bool bf16) {
+  const void* fn = bf16 ? tv_kernel_ptr<uint16_t, true>() : tv_kernel_ptr<float, true>();
+  int res = resident_wgs(fn, bf16 ? 0 : 2);
+  if (res > 64) res = 64;
+  return res * CHUNK;
+}
+
+hipError_t launch_tv(const TvArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(tv_count_kernel, dim3(1), dim3(1024), 0, stream, a.mask, a.R, a.ws, a.loss);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.R == 0) return e;
+  if (a.bf16) {
+    const bool vec = tv_rows_aligned<uint16_t>(a.teacher, a.V) && tv_rows_aligned<uint16_t>(a.student, a.V) &&
+                     (!a.grad || tv_rows_aligned<uint16_t>(a.grad, a.V));
+    return vec ? launch_tv_t<uint16_t, true>(a, 0, stream) : launch_tv_t<uint16_t, false>(a, 1, stream);
+  }
+  const bool vec = tv_rows_aligned<float>(a.teacher, a.V) && tv_rows_aligned<float>(a.student, a.V) &&
+                   (!a.grad || tv_rows_aligned<float>(a.grad, a.V));
+  return vec ? launch_tv_t<float, true>(a, 2, stream) : launch_tv_t<float, false>(a, 3, stream);
+}
+
+}  // namespace uno

@@ -75,3 +75,22 @@ def test_product_package_never_imports_the_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle", src, re.M), f
                 assert "oracle/" not in src, f
+
+
+def _tv(lib, R=4, V=1024, dtype=1, T=1.0, loss=True, ws=1 << 24, null_ws=False):
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    return lib.uno_tv_loss_fwd_bwd(fake, fake, dtype, fake, R, V, T, fake if loss else None, None, None,
+                                   None if null_ws else fake, ws, None)
+
+
+def test_tv_argument_validation(lib):
+    assert _tv(lib, R=-1) == _lib.UNO_ERR_INVALID_ARG
+    assert _tv(lib, V=0) == _lib.UNO_ERR_INVALID_ARG
+    assert _tv(lib, T=0.0) == _lib.UNO_ERR_INVALID_ARG
+    assert _tv(lib, T=float("nan")) == _lib.UNO_ERR_INVALID_ARG
+    assert _tv(lib, T=float("inf")) == _lib.UNO_ERR_INVALID_ARG
+    assert _tv(lib, dtype=5) == _lib.UNO_ERR_INVALID_ARG
+    assert _tv(lib, loss=False) == _lib.UNO_ERR_INVALID_ARG
+    assert _tv(lib, ws=64) == _lib.UNO_ERR_WORKSPACE
+    assert _tv(lib, null_ws=True) == _lib.UNO_ERR_WORKSPACE
+    assert lib.uno_tv_loss_workspace(32768, 151936) >= 32768 * 8

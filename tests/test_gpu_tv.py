@@ -1,0 +1,196 @@
+"""GPU parity of the fused TV self-distillation loss (forward + student gradient)
+against the fp64 CPU oracle.
+
+Tolerances: the loss and the per-row TV are fp32 results of fp32 exponentials
+summed partly in fp64, so they must agree with the oracle to 1e-5 relative (with
+a 2e-6 absolute floor for rows whose TV is near zero). The gradient is stored in
+the logits' dtype; for bf16 its rounding alone is 2^-9 relative per element, so
+the check is normwise: per row and over all compared rows,
+||g - g_ref|| <= 2e-2 ||g_ref||. Rows outside the response mask must be exactly 0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import to_device
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import lossless_diffusion_drafted_amd as uno
+    uno.load()
+
+
+def _uno():
+    import lossless_diffusion_drafted_amd as uno
+    return uno
+
+
+def _inputs(R, V, dtype, seed):
+    if dtype == "bf16":
+        return workloads.tv_rows(range(R), V, seed=seed)
+    rng = np.random.default_rng([seed, R, V])
+    t = (3.0 * rng.standard_normal((R, V))).astype(np.float32)
+    s = (t + rng.standard_normal((R, V))).astype(np.float32)
+    return t, s
+
+
+def _run(t, s, mask, T, want_grad=True, want_rows=True):
+    uno = _uno()
+    loss, rows, grad = uno.uno_tv_loss_fwd_bwd(to_device(t, DEV), to_device(s, DEV), to_device(mask, DEV),
+                                               temperature=T, want_grad=want_grad, want_rows=want_rows)
+    torch.cuda.synchronize()
+    out = {"loss": float(loss.item())}
+    out["rows"] = rows.cpu().numpy().astype(np.float64) if rows is not None else None
+    out["grad"] = grad.float().cpu().numpy().astype(np.float64) if grad is not None else None
+    return out
+
+
+def _check(gpu, ref_loss, ref_rows, ref_grad, mask, T=1.0):
+    assert abs(gpu["loss"] - ref_loss) <= 1e-5 * abs(ref_loss) + 2e-6, (gpu["loss"], ref_loss)
+    if gpu["rows"] is not None:
+        np.testing.assert_allclose(gpu["rows"], ref_rows, rtol=1e-5, atol=2e-6)
+        assert np.all(gpu["rows"][mask == 0] == 0.0)
+    if gpu["grad"] is not None and ref_grad is not None:
+        g, gr = gpu["grad"], ref_grad
+        assert np.all(g[mask == 0] == 0.0)
+        for r in np.flatnonzero(mask):
+            nr = np.linalg.norm(gr[r])
+            if nr > 0:
+                assert np.linalg.norm(g[r] - gr[r]) <= 2e-2 * nr, r
+            else:
+                assert np.all(g[r] == 0.0), r
+        nt = np.linalg.norm(gr)
+        assert np.linalg.norm(g - gr) <= 2e-2 * nt + 1e-30
+        # the loss is invariant to shifting a row's logits, so each gradient row sums
+        # to 0 up to rounding: the terms q_j (s_j/2 - G) / (T N) cancel with an error of
+        # about eps32 / (T N), and the bf16 rounding adds 2^-9 of sum |g| at most
+        n = max(int(mask.sum()), 1)
+        sums = np.abs(g.sum(axis=1))
+        assert np.all(sums <= 2 ** -8 * np.abs(g).sum(axis=1) + 1e-6 / (T * n))
+
+
+@pytest.mark.parametrize("R,V,dtype,T,mask_kind", [
+    (5, 1000, "bf16", 1.0, "all"),        # one workgroup per row, few teams
+    (16, 1000, "bf16", 1.0, "random"),
+    (40, 50000, "bf16", 0.7, "random"),   # three-workgroup row teams, ragged last slice
+    (13, 50000, "f32", 1.0, "random"),    # more rows than teams of this size fit per pass
+    (9, 30001, "f32", 1.3, "all"),        # rows not 16-byte aligned
+    (7, 4097, "bf16", 1.0, "random"),     # rows not 16-byte aligned
+    (6, 151936, "bf16", 1.0, "all"),      # the full vocabulary: eight-workgroup teams
+    (3, 163840, "bf16", 1.0, "all"),      # exactly fills eight slices
+])
+def test_tv_matches_oracle(R, V, dtype, T, mask_kind):
+    t, s = _inputs(R, V, dtype, seed=R * 7 + V)
+    if mask_kind == "all":
+        mask = np.ones(R, np.uint8)
+    else:
+        mask = (np.random.default_rng(R + V).random(R) < 0.7).astype(np.uint8)
+        mask[0] = 1
+    ref_loss, ref_rows, ref_grad = oracle.tv_loss_fwd_bwd(t, s, mask, T, dtype=dtype)
+    gpu = _run(t, s, mask, T)
+    _check(gpu, ref_loss, ref_rows, ref_grad, mask, T)
+
+
+def test_tv_forward_only_and_optional_rows():
+    t, s = _inputs(12, 20000, "bf16", seed=3)
+    mask = np.ones(12, np.uint8)
+    ref_loss, ref_rows, _ = oracle.tv_loss_fwd_bwd(t, s, mask, 1.0, dtype="bf16", want_grad=False)
+    gpu = _run(t, s, mask, 1.0, want_grad=False, want_rows=True)
+    _check(gpu, ref_loss, ref_rows, None, mask)
+    gpu = _run(t, s, mask, 1.0, want_grad=True, want_rows=False)
+    assert abs(gpu["loss"] - ref_loss) <= 1e-5 * ref_loss + 2e-6
+
+
+def test_tv_no_response_rows():
+    t, s = _inputs(6, 3000, "bf16", seed=5)
+    mask = np.zeros(6, np.uint8)
+    gpu = _run(t, s, mask, 1.0)
+    assert gpu["loss"] == 0.0
+    assert np.all(gpu["rows"] == 0.0) and np.all(gpu["grad"] == 0.0)
+
+
+def test_tv_empty_batch():
+    uno = _uno()
+    z = torch.empty((0, 100), dtype=torch.bfloat16, device=DEV)
+    m = torch.empty((0,), dtype=torch.uint8, device=DEV)
+    loss, rows, grad = uno.uno_tv_loss_fwd_bwd(z, z, m)
+    torch.cuda.synchronize()
+    assert loss.item() == 0.0
+
+
+def test_tv_identical_and_disjoint_rows():
+    """p = q gives TV 0 and an exactly zero gradient; almost disjoint one-hot rows give TV ~ 1."""
+    V = 70000
+    t, _ = _inputs(4, V, "bf16", seed=9)
+    s = t.copy()
+    big = workloads.to_bf16_bits(np.array([60.0], np.float32))[0]
+    s[2] = workloads.to_bf16_bits(np.zeros(V, np.float32))
+    t2 = s[2].copy()
+    t2[11] = big
+    s[2, 12] = big
+    t[2] = t2
+    mask = np.ones(4, np.uint8)
+    ref_loss, ref_rows, ref_grad = oracle.tv_loss_fwd_bwd(t, s, mask, 1.0, dtype="bf16")
+    gpu = _run(t, s, mask, 1.0)
+    for r in (0, 1, 3):
+        assert gpu["rows"][r] == 0.0
+        assert np.all(gpu["grad"][r] == 0.0)
+    assert abs(gpu["rows"][2] - 1.0) < 1e-6 and abs(ref_rows[2] - 1.0) < 1e-6
+    _check(gpu, ref_loss, ref_rows, ref_grad, mask)
+
+
+def test_tv_repeat_runs_are_identical():
+    t, s = _inputs(24, 40000, "bf16", seed=11)
+    mask = np.ones(24, np.uint8)
+    uno = _uno()
+    td, sd, md = to_device(t, DEV), to_device(s, DEV), to_device(mask, DEV)
+    first = None
+    for _ in range(3):
+        loss, rows, grad = uno.uno_tv_loss_fwd_bwd(td, sd, md)
+        cur = (loss.clone(), rows.clone(), grad.clone())
+        if first is None:
+            first = cur
+        else:
+            for a, b in zip(cur, first):
+                assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                                   b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+
+
+def test_tv_full_size_sampled_rows():
+    """The self-distillation workload at full size (8 x 4096 rows, V = 151936, bf16):
+    sampled rows against the oracle, every unmasked row exactly zero, and the loss
+    equal to the mean of the per-row TVs."""
+    cfg = workloads.TV_CONFIG
+    V = cfg["V"]
+    R = cfg["n_seq"] * cfg["seq_len"]
+    uno = _uno()
+    t, s = workloads.tv_inputs_torch(R, V, DEV, seed=0)
+    mask_np = workloads.tv_response_mask(cfg["n_seq"], cfg["seq_len"], cfg["resp_len"])
+    mask = to_device(mask_np, DEV)
+    loss, rows, grad = uno.uno_tv_loss_fwd_bwd(t, s, mask, temperature=1.0)
+    torch.cuda.synchronize()
+    rows_np = rows.cpu().numpy().astype(np.float64)
+    n = int(mask_np.sum())
+    assert abs(loss.item() - rows_np[mask_np == 1].sum() / n) <= 1e-6 * loss.item()
+    assert 0.3 < loss.item() < 0.5
+    assert np.all(rows_np[mask_np == 0] == 0.0)
+    unmasked = torch.from_numpy(mask_np == 0).to(DEV)
+    assert int(torch.count_nonzero(grad[unmasked])) == 0
+    sample = [1024, 1025, 4095, 9000, 17555, 24576 + 1023 + 1, R - 1]
+    sample = [r for r in sample if mask_np[r]]
+    tt = t[sample].view(torch.int16).cpu().numpy().view(np.uint16)
+    ss = s[sample].view(torch.int16).cpu().numpy().view(np.uint16)
+    _, ref_rows, ref_grad = oracle.tv_loss_fwd_bwd(tt, ss, np.ones(len(sample), np.uint8), 1.0, dtype="bf16")
+    ref_grad *= len(sample) / n              # the oracle normalised by the sample's row count
+    np.testing.assert_allclose(rows_np[sample], ref_rows, rtol=1e-5, atol=2e-6)
+    g = grad[sample].float().cpu().numpy().astype(np.float64)
+    for a in range(len(sample)):
+        assert np.linalg.norm(g[a] - ref_grad[a]) <= 2e-2 * np.linalg.norm(ref_grad[a])
