@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdint.h>
 #include <string.h>
 
 #include "../../include/uno.h"
@@ -199,16 +200,48 @@ int uno_tv_loss_fwd_bwd(const void* teacher_logits, const void* student_logits, 
 }
 
 size_t uno_gated_lora_linear_workspace(int M, int N, int K, int r) {
-  (void)M;
-  (void)N;
-  (void)K;
-  (void)r;
-  return 256;
+  if (M <= 0 || N <= 0 || K <= 0 || r < 0) return 256;
+  return uno::gemm_workspace_bytes(M, N, K, r);
 }
 
-int uno_gated_lora_linear(const void*, const void*, const void*, const void*, const uint8_t*,
-                          float, void*, int, int, int, int, void*, size_t, void*) {
-  return fail(UNO_ERR_UNSUPPORTED, "uno_gated_lora_linear: not built yet");
+int uno_gated_lora_linear(const void* X, const void* W, const void* A, const void* B,
+                          const uint8_t* row_mask, float scale, void* Y, int M, int N, int K, int r,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "uno_gated_lora_linear";
+  if (M < 0 || N < 0 || K < 1 || r < 0)
+    return fail(UNO_ERR_INVALID_ARG, "%s: sizes M = %d, N = %d, K = %d, r = %d out of range", fn, M, N, K, r);
+  if (!isfinite(scale)) return fail(UNO_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (M == 0 || N == 0) return ok();
+  if (!X || !W || !Y) return fail(UNO_ERR_INVALID_ARG, "%s: X, W and Y must not be null", fn);
+  if (r > 0 && (!A || !B || !row_mask))
+    return fail(UNO_ERR_INVALID_ARG, "%s: A, B and row_mask must not be null when r > 0", fn);
+  if (K % 8 != 0 || r % 8 != 0)
+    return fail(UNO_ERR_UNSUPPORTED, "%s: K = %d and r = %d must be multiples of 8", fn, K, r);
+  const void* ptrs[4] = {X, W, A, B};
+  for (int i = 0; i < 4; ++i)
+    if (ptrs[i] && reinterpret_cast<uintptr_t>(ptrs[i]) % 16 != 0)
+      return fail(UNO_ERR_UNSUPPORTED, "%s: operand %d is not 16-byte aligned", fn, i);
+  const long long lim = 0x7fffffffLL;
+  if ((long long)M * K * 2 > lim || (long long)N * K * 2 > lim || (long long)M * N > lim ||
+      (long long)N * r * 2 > lim)
+    return fail(UNO_ERR_UNSUPPORTED, "%s: an operand exceeds 2 GiB", fn);
+  const size_t need = uno_gated_lora_linear_workspace(M, N, K, r);
+  if (r > 0 && (!workspace || ws_bytes < need))
+    return fail(UNO_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, need);
+  uno::GemmArgs a;
+  a.X = X;
+  a.W = W;
+  a.A = A;
+  a.B = B;
+  a.row_mask = row_mask;
+  a.scale = scale;
+  a.Y = Y;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.r = r;
+  a.ws = workspace;
+  return hip_status(uno::launch_gemm(a, static_cast<hipStream_t>(stream)), "uno_gated_lora_linear launch");
 }
 
 }  // extern "C"

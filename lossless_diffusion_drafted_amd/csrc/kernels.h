@@ -55,6 +55,18 @@ struct TvArgs {
   void* ws;
 };
 
+struct GemmArgs {
+  const void* X;
+  const void* W;
+  const void* A;
+  const void* B;
+  const uint8_t* row_mask;
+  float scale;
+  void* Y;
+  int M, N, K, r;
+  void* ws;
+};
+
 // Largest top-k the single-pass selection handles, and largest vocabulary that
 // may be taken whole when top-k is off.
 constexpr int kVerifyKMaxFast = 256;
@@ -66,6 +78,8 @@ hipError_t launch_draft(const DraftArgs& a, hipStream_t stream);
 size_t tv_workspace_bytes(int R);
 int tv_max_vocab(bool bf16);          // largest V one row team covers on this device
 hipError_t launch_tv(const TvArgs& a, hipStream_t stream);
+size_t gemm_workspace_bytes(int M, int N, int K, int r);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t stream);
 
 }  // namespace uno
