@@ -54,15 +54,16 @@ __device__ __forceinline__ uint4 load_chunk(__amdgpu_buffer_rsrc_t rs, uint32_t 
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// One operand tile: rows r0..r0+127 of a [rows, k] matrix, columns k0..k0+63.
-__device__ __forceinline__ void load_tile(const uint16_t* base, int rows, int k, int r0, int k0,
+// One operand tile: rows r0..r0+127 of a [rows, k] matrix, columns k0..k0+63;
+// columns at or past `kk` (k, or 0 for a tile past the end) read zero.
+__device__ __forceinline__ void load_tile(const uint16_t* base, int rows, int k, int r0, int k0, int kk,
                                           uint4 (&reg)[LOADS]) {
   const __amdgpu_buffer_rsrc_t rs = make_row_rsrc(base, uint32_t(size_t(rows) * size_t(k) * 2u));
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int c = int(threadIdx.x) + i * GT;
     const int row = c >> 3, col = (c & 7) * 8;
-    const bool ok = (r0 + row < rows) && (k0 + col < k);
+    const bool ok = (r0 + row < rows) && (k0 + col < kk);
     reg[i] = load_chunk(rs, uint32_t((size_t(r0 + row) * size_t(k) + size_t(k0 + col)) * 2u), ok);
   }
 }
@@ -92,16 +93,14 @@ __global__ __launch_bounds__(GT) void gemm_kernel(GemmParams p) {
   const int n1tiles = p.nseg > 1 ? (p.seg[1].k + BK - 1) / BK : 0;
   const int ntiles = n0tiles + n1tiles;
 
+  // Tiles at or past the end are fetched with out-of-range offsets (zeros, no
+  // memory traffic), so every step issues the same loads without branches.
   auto fetch = [&](int t, uint4 (&ra)[LOADS], uint4 (&rb)[LOADS]) {
-    if (t < n0tiles) {
-      const int k0 = (t_begin + t) * BK;
-      load_tile(p.seg[0].a, p.M, p.seg[0].k, m0, k0, ra);
-      load_tile(p.seg[0].b, p.N, p.seg[0].k, n0, k0, rb);
-    } else {
-      const int k0 = (t - n0tiles) * BK;
-      load_tile(p.seg[1].a, p.M, p.seg[1].k, m0, k0, ra);
-      load_tile(p.seg[1].b, p.N, p.seg[1].k, n0, k0, rb);
-    }
+    const Seg& sg = t < n0tiles ? p.seg[0] : p.seg[p.nseg - 1];
+    const int k0 = t < n0tiles ? (t_begin + t) * BK : (t - n0tiles) * BK;
+    const int kk = t < ntiles ? sg.k : 0;
+    load_tile(sg.a, p.M, sg.k, m0, k0, kk, ra);
+    load_tile(sg.b, p.N, sg.k, n0, k0, kk, rb);
   };
 
   f32x16_t acc[2][2];
@@ -112,22 +111,10 @@ __global__ __launch_bounds__(GT) void gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  uint4 ra[LOADS], rb[LOADS];
-  if (ntiles > 0) {
-    fetch(0, ra, rb);
-    store_tile(lds[0][0], ra);
-    store_tile(lds[0][1], rb);
-  }
-  __syncthreads();
-
   // Fragment addresses: lane l holds row (l % 32) and k = 8 (l / 32) .. +7 of
   // each 32 x 16 slice.
   const int frow = lane & 31, fk = (lane >> 5) * 8;
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) fetch(t + 1, ra, rb);
-    const uint16_t* As = lds[buf][0];
-    const uint16_t* Bs = lds[buf][1];
+  auto compute = [&](const uint16_t* As, const uint16_t* Bs) {
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       bf16x8_t af[2], bfr[2];
@@ -143,11 +130,29 @@ __global__ __launch_bounds__(GT) void gemm_kernel(GemmParams p) {
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (t + 1 < ntiles) {
-      store_tile(lds[buf ^ 1][0], ra);
-      store_tile(lds[buf ^ 1][1], rb);
-    }
+  };
+
+  // Two register stages: the loads of tile t+2 are in flight while tile t is
+  // multiplied out of LDS and tile t+1 waits in registers.
+  uint4 ra0[LOADS], rb0[LOADS], ra1[LOADS], rb1[LOADS];
+  fetch(0, ra0, rb0);
+  fetch(1, ra1, rb1);
+  store_tile(lds[0][0], ra0);
+  store_tile(lds[0][1], rb0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    fetch(t + 2, ra0, rb0);
+    compute(lds[0][0], lds[0][1]);
+    store_tile(lds[1][0], ra1);
+    store_tile(lds[1][1], rb1);
     __syncthreads();
+    if (t + 1 < ntiles) {
+      fetch(t + 3, ra1, rb1);
+      compute(lds[1][0], lds[1][1]);
+      store_tile(lds[0][0], ra0);
+      store_tile(lds[0][1], rb0);
+      __syncthreads();
+    }
   }
 
   // Epilogue. Accumulator v of a 32 x 32 block sits at row 8 (v / 4) + 4 (l / 32)
