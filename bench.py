@@ -14,9 +14,20 @@ self-distillation workload (8 x 4096 rows, vocabulary 151936) as a separate leg,
 and the CPU oracle timed on a bounded sample of the same verify workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-tv]
+
+Counter runs (rocprofv3 --pmc) time one kernel alone:
+  python bench.py --only {verify,gemm_attn,gemm_mlp,tv,copy} --steps K
+where `copy` is a plain 1 GiB elementwise copy (torch.neg) that calibrates the
+FETCH_SIZE / WRITE_SIZE counters. `--summarize-pmc DIR --kernel NAME` turns the
+four counter CSVs of such runs (DIR/{fetch,write,copy_fetch,copy_write}) into the
+text summary profiles/NAME_traffic.md, which the benchmark line then reads for
+its `traffic` figure as long as the kernel's source is unchanged.
 """
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +39,17 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
+COPY_BYTES = 1 << 30            # size of the calibration copy
+
+# Source file of each timed entry point (the traffic summary is tied to its hash).
+KERNEL_SOURCES = {
+    "verify": "lossless_diffusion_drafted_amd/csrc/verify.hip",
+    "gated_lora_attn_4096x4096": "lossless_diffusion_drafted_amd/csrc/gemm.hip",
+    "gated_lora_mlp_4096x12288": "lossless_diffusion_drafted_amd/csrc/gemm.hip",
+    "tv": "lossless_diffusion_drafted_amd/csrc/tv.hip",
+}
+ONLY = {"verify": "verify", "gemm_attn": "gated_lora_attn_4096x4096",
+        "gemm_mlp": "gated_lora_mlp_4096x12288", "tv": "tv"}
 
 
 def parse():
@@ -37,6 +59,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-tv", action="store_true", help="skip the TV-loss leg")
+    ap.add_argument("--only", choices=sorted(list(ONLY) + ["copy"]),
+                    help="run one kernel alone (for counter runs) and print its timing")
+    ap.add_argument("--summarize-pmc", metavar="DIR", help="write profiles/KERNEL_traffic.md from counter CSVs")
+    ap.add_argument("--kernel", help="timed entry point the counter CSVs belong to (with --summarize-pmc)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="minimum CPU time spent on the oracle sample")
     return ap.parse_args()
@@ -79,27 +105,38 @@ def verify_bytes(S, b, V, esize=2):
     return (S * b + S * (b - 1)) * V * esize + S * b * 4 * 2 + S * 16 + S * 8
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path "
-                         "(run with --gpus 1)\n")
-        sys.exit(2)
+def source_sha256(name):
+    path = os.path.join(ROOT, KERNEL_SOURCES[name])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
+
+def traffic_from_profile(name):
+    """HBM bytes per call from profiles/NAME_traffic.md, or None when the summary is
+    missing or was taken on a different version of the kernel's source."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].strip().split(": ", 1)
+                vals[k.strip("`")] = v.strip().strip("`")
+    if vals.get("source_sha256") != source_sha256(name):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+def setup_verify(uno, workloads, dev):
     import numpy as np
     import torch
-
-    import lossless_diffusion_drafted_amd as uno
-    import workloads
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    uno.load()
     sp = workloads.SAMPLING
     cfg = workloads.VERIFY_CONFIGS["qwen"]
-    S, b, V = cfg["S"], cfg["b"], cfg["V"]
-
-    # --- inputs resident in HBM -------------------------------------------------
+    S, b = cfg["S"], cfg["b"]
     p_np, q_np = workloads.verify_logits("qwen")
     p, q = dev_tensor(p_np, dev), dev_tensor(q_np, dev)
     seq = dev_tensor(np.arange(S, dtype=np.int64), dev)
@@ -109,34 +146,172 @@ def main():
                 accept_len=torch.empty((S,), dtype=torch.int32, device=dev),
                 resampled=torch.empty((S,), dtype=torch.int32, device=dev))
 
+    def run():
+        return uno.uno_verify_block(p, q, draft, seq, pos, want_slot_accept=False, want_diag=False,
+                                    out=outs, **sp)
+    return run, outs, (p_np, q_np)
+
+
+def setup_gemms(uno, workloads, dev):
+    import torch
     gcfg = workloads.GEMM_CONFIGS["qwen"]
     M, r = gcfg["M"], gcfg["r"]
-    mask = dev_tensor(workloads.noise_row_mask(S, b), dev)
-    gemms = []
+    mask = dev_tensor(workloads.noise_row_mask(M // gcfg["b"], gcfg["b"]), dev)
+    runs = {}
     for gi, (name, K, N) in enumerate(gcfg["projections"]):
         X, W, A, B = workloads.gemm_inputs(M, K, N, r, tag=gi)
+        X, W, A, B = (dev_tensor(a, dev) for a in (X, W, A, B))
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        gemms.append((name, K, N, dev_tensor(X, dev), dev_tensor(W, dev), dev_tensor(A, dev),
-                      dev_tensor(B, dev), Y))
-    gemm_ok = True
-    try:
-        g = gemms[0]
-        uno.uno_gated_lora_linear(g[3], g[4], g[5], g[6], mask, 1.0, out=g[7])
-    except uno.UnoError as e:
-        if e.status != "UNO_ERR_UNSUPPORTED":
-            raise
-        gemm_ok = False
+        runs[f"gated_lora_{name}"] = (
+            lambda X=X, W=W, A=A, B=B, Y=Y: uno.uno_gated_lora_linear(X, W, A, B, mask, 1.0, out=Y),
+            2.0 * M * N * K + 2.0 * M * K * r + 2.0 * M * r * N)
+    return runs
+
+
+def run_only(args, uno, workloads, dev):
+    """One kernel alone, for counter runs: prints its average time per call."""
+    import torch
+    timer = KernelTimer()
+    if args.only == "copy":
+        # an elementwise kernel that reads and writes COPY_BYTES once each
+        src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        fn = lambda: torch.neg(src, out=dst)
+    elif args.only == "verify":
+        fn, _, _ = setup_verify(uno, workloads, dev)
+    elif args.only == "tv":
+        c = workloads.TV_CONFIG
+        R, V = c["n_seq"] * c["seq_len"], c["V"]
+        t, s = workloads.tv_inputs_torch(R, V, dev)
+        mask = torch.from_numpy(workloads.tv_response_mask(c["n_seq"], c["seq_len"], c["resp_len"])).to(dev)
+        fn = lambda: uno.uno_tv_loss_fwd_bwd(t, s, mask, c["temperature"], want_rows=False)
+    else:
+        fn = setup_gemms(uno, workloads, dev)[ONLY[args.only]][0]
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        timer.run(args.only, fn)
+    torch.cuda.synchronize()
+    print(json.dumps({"only": args.only, "calls": args.steps, "avg_us": timer.avg_ms(args.only) * 1000}))
+
+
+def summarize_pmc(directory, name):
+    """profiles/NAME_traffic.md from four counter runs under DIRECTORY: the kernel's
+    FETCH_SIZE and WRITE_SIZE runs (pmc_ONLY/fetch, pmc_ONLY/write) and the copy's
+    (pmc_copy/copy_fetch, pmc_copy/copy_write), each a rocprofv3 --pmc CSV."""
+    only = [k for k, v in ONLY.items() if v == name][0]
+
+    def per_call(sub, counter, copy):
+        files = glob.glob(os.path.join(directory, sub, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {os.path.join(directory, sub)}")
+        total, dispatches, kernels = 0.0, set(), {}
+        for fpath in files:
+            with open(fpath) as f:
+                for row in csv.DictReader(f):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    kname = row.get("Kernel_Name", "")
+                    if copy != ("uno::" not in kname):
+                        continue
+                    if copy and "neg" not in kname:
+                        continue
+                    v = float(row["Counter_Value"])
+                    total += v
+                    dispatches.add(row.get("Dispatch_Id"))
+                    short = kname.split("(")[0].replace("uno::(anonymous namespace)::", "")
+                    kernels[short] = kernels.get(short, 0.0) + v
+        return total, len(dispatches), kernels
+
+    calls = int(os.environ.get("PMC_CALLS", "0"))
+    if calls <= 0:
+        raise SystemExit("set PMC_CALLS to the number of timed calls in the kernel runs (warmup + steps)")
+    copy_calls = int(os.environ.get("PMC_COPY_CALLS", str(calls)))
+    f_kib, f_n, f_k = per_call(f"pmc_{only}/fetch", "FETCH_SIZE", False)
+    w_kib, w_n, w_k = per_call(f"pmc_{only}/write", "WRITE_SIZE", False)
+    cf_kib, _, _ = per_call("pmc_copy/copy_fetch", "FETCH_SIZE", True)
+    cw_kib, _, _ = per_call("pmc_copy/copy_write", "WRITE_SIZE", True)
+    # bytes per KiB-count, from the copy of known size (each copy reads and writes COPY_BYTES)
+    f_scale = COPY_BYTES * copy_calls / cf_kib
+    w_scale = COPY_BYTES * copy_calls / cw_kib
+    fetch = f_kib * f_scale / calls
+    write = w_kib * w_scale / calls
+    out = os.path.join(ROOT, "profiles", f"{name}_traffic.md")
+    with open(out, "w") as f:
+        f.write(f"# HBM traffic of `{name}` (rocprofv3 counters)\n\n")
+        f.write("Commands (from the repository root on the GPU box, `cd /tmp && export TMPDIR=/tmp` first,\n"
+                "R = the repository path):\n\n")
+        for sub, ctr, what in (("fetch", "FETCH_SIZE", only), ("write", "WRITE_SIZE", only),
+                               ("copy_fetch", "FETCH_SIZE", "copy"), ("copy_write", "WRITE_SIZE", "copy")):
+            f.write(f"    timeout -s KILL 120 rocprofv3 --pmc {ctr} --output-format csv "
+                    f"-d $R/gpurun_out/pmc_{what}/{sub} -o {sub} -- "
+                    f"python3 $R/bench.py --only {what} --steps {calls - 1 if what != 'copy' else copy_calls - 1} "
+                    f"--warmup 1\n")
+        f.write(f"    PMC_CALLS={calls} PMC_COPY_CALLS={copy_calls} python3 bench.py --summarize-pmc gpurun_out "
+                f"--kernel {name}\n\n")
+        f.write("Counters are summed over every dispatch of the library's kernels in the run and divided by\n"
+                "the number of calls. The KiB counts are scaled by the copy calibration: a plain\n"
+                f"elementwise copy (torch.neg) of {COPY_BYTES} B reads and writes exactly that many bytes.\n\n")
+        f.write(f"- source: `{KERNEL_SOURCES[name]}`\n")
+        f.write(f"- source_sha256: `{source_sha256(name)}`\n")
+        f.write(f"- calls: {calls}\n")
+        f.write(f"- fetch_kib_per_call: {f_kib / calls:.1f}\n")
+        f.write(f"- write_kib_per_call: {w_kib / calls:.1f}\n")
+        f.write(f"- copy_fetch_kib_per_copy: {cf_kib / copy_calls:.1f}\n")
+        f.write(f"- copy_write_kib_per_copy: {cw_kib / copy_calls:.1f}\n")
+        f.write(f"- fetch_scale_bytes_per_kib: {f_scale:.2f}\n")
+        f.write(f"- write_scale_bytes_per_kib: {w_scale:.2f}\n")
+        f.write(f"- hbm_fetch_bytes_per_call: {fetch:.0f}\n")
+        f.write(f"- hbm_write_bytes_per_call: {write:.0f}\n")
+        f.write(f"- hbm_bytes_per_call: {fetch + write:.0f}\n\n")
+        f.write("Per-kernel FETCH_SIZE / WRITE_SIZE (KiB per call):\n\n")
+        for k in sorted(set(f_k) | set(w_k)):
+            f.write(f"    {k}: fetch {f_k.get(k, 0.0) / calls:.1f}  write {w_k.get(k, 0.0) / calls:.1f}\n")
+    print(out)
+
+
+def main():
+    args = parse()
+    if args.summarize_pmc:
+        if args.kernel not in KERNEL_SOURCES:
+            raise SystemExit(f"--kernel must be one of {sorted(KERNEL_SOURCES)}")
+        summarize_pmc(args.summarize_pmc, args.kernel)
+        return
+    if args.gpus != 1:
+        sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path "
+                         "(run with --gpus 1)\n")
+        sys.exit(2)
+
+    import torch
+
+    import lossless_diffusion_drafted_amd as uno
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    uno.load()
+    if args.only:
+        run_only(args, uno, workloads, dev)
+        return
+
+    sp = workloads.SAMPLING
+    cfg = workloads.VERIFY_CONFIGS["qwen"]
+    S, b, V = cfg["S"], cfg["b"], cfg["V"]
+    gcfg = workloads.GEMM_CONFIGS["qwen"]
+    M, r = gcfg["M"], gcfg["r"]
+
+    # --- inputs resident in HBM -------------------------------------------------
+    verify_run, outs, (p_np, q_np) = setup_verify(uno, workloads, dev)
+    gemms = setup_gemms(uno, workloads, dev)
     torch.cuda.synchronize()
 
     timer = KernelTimer()
 
     def step():
-        if gemm_ok:
-            for (name, K, N, X, W, A, B, Y) in gemms:
-                timer.run(f"gated_lora_{name}",
-                          lambda X=X, W=W, A=A, B=B, Y=Y: uno.uno_gated_lora_linear(X, W, A, B, mask, 1.0, out=Y))
-        timer.run("verify", lambda: uno.uno_verify_block(p, q, draft, seq, pos, want_slot_accept=False,
-                                                          want_diag=False, out=outs, **sp))
+        for name, (fn, _) in gemms.items():
+            timer.run(name, fn)
+        timer.run("verify", verify_run)
 
     for _ in range(args.warmup):
         step()
@@ -157,22 +332,20 @@ def main():
     kernels["verify"] = dict(avg_us=t_ver * 1000, bytes=vb, GBps=vb / (t_ver * 1e6),
                              hbm_frac=vb / (t_ver * 1e6) / HBM_PEAK_GBS,
                              positions_per_s=positions / (t_ver / 1000))
-    if gemm_ok:
-        for (name, K, N, *_rest) in gemms:
-            t = timer.avg_ms(f"gated_lora_{name}")
-            flops = 2.0 * M * N * K + 2.0 * M * K * r + 2.0 * M * r * N
-            kernels[f"gated_lora_{name}"] = dict(avg_us=t * 1000, flops=flops,
-                                                 TFLOPs=flops / (t * 1e9),
-                                                 mfma_frac=flops / (t * 1e9) / BF16_PEAK_TFLOPS)
+    for name, (_, flops) in gemms.items():
+        t = timer.avg_ms(name)
+        kernels[name] = dict(avg_us=t * 1000, flops=flops, TFLOPs=flops / (t * 1e9),
+                             mfma_frac=flops / (t * 1e9) / BF16_PEAK_TFLOPS)
     acc = outs["accept_len"].float()
     dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    traffic = traffic_from_profile(dominant)
     if dominant == "verify":
         roof = dict(bound="hbm", achieved=kernels["verify"]["GBps"], peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=kernels["verify"]["hbm_frac"], traffic=None, kernel="verify")
+                    frac=kernels["verify"]["hbm_frac"], traffic=traffic, kernel="verify")
     else:
         k = kernels[dominant]
         roof = dict(bound="mfma", achieved=k["TFLOPs"], peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=k["mfma_frac"], traffic=None, kernel=dominant)
+                    frac=k["mfma_frac"], traffic=traffic, kernel=dominant)
 
     tv_leg = None
     if not args.no_tv:
@@ -197,9 +370,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": "qwen3-8b-shaped verify step: 64 seq x block 16, V=151936 bf16 logits, "
                                "T=1.0 top-k 50 top-p 0.95; gated LoRA r=128 on 4096x4096 and "
-                               "4096x12288 over 1024 rows" + ("" if gemm_ok else " (gated LoRA not built: verify only)"),
+                               "4096x12288 over 1024 rows",
                    "S": S, "block": b, "vocab": V, "gemm_rows": M, "rank": r,
-                   "step": (["gated_lora_attn_4096x4096", "gated_lora_mlp_4096x12288"] if gemm_ok else []) + ["verify"]},
+                   "step": list(gemms) + ["verify"]},
         "roofline": roof,
         "kernels": kernels,
         "mean_accept_len": acc.mean().item(),
