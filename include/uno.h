@@ -114,10 +114,11 @@ int uno_workspace_init(void* workspace, size_t bytes, void* stream);
  *                        flag bits (UNO_FLAG_*)
  *   workspace          : >= uno_verify_block_workspace(S, b, V) bytes, zeroed once
  * Limits: 1 <= b <= 64, 1 <= V < 2^31, S >= 0 (S == 0 launches nothing).
- * Rows whose filtered support is larger than 256 tokens, or top-k off / k > 256
- * with V > 2048, are not handled by this build: their slot gets UNO_FLAG_OVERFLOW
- * and token -1 (the call returns UNO_ERR_UNSUPPORTED up front when the settings
- * alone make every row such a row).
+ * Every setting is handled: top-k up to 128 (or any top-k when V <= 256) takes
+ * a single pass over the logits; top-k off, larger top-k, and rows whose
+ * candidate list or tie-inclusive top-k set outgrows the single pass take a
+ * multi-pass full-row path (same results, slower). UNO_FLAG_OVERFLOW is no
+ * longer produced.
  * ------------------------------------------------------------------------- */
 size_t uno_verify_block_workspace(int S, int b, int V);
 int uno_verify_block(const void* p_logits, const void* q_logits, int dtype,

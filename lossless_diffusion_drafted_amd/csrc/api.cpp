@@ -50,13 +50,6 @@ int check_sampling(const uno_sampling_params& sp, int S, int b, int V, const cha
     return fail(UNO_ERR_INVALID_ARG, "%s: S * b = %lld slots exceeds 2^31 - 1", fn, (long long)S * b);
   if (isnan(sp.temperature)) return fail(UNO_ERR_INVALID_ARG, "%s: temperature is NaN", fn);
   if (!(sp.top_p > 0.0)) return fail(UNO_ERR_INVALID_ARG, "%s: top_p must be > 0 (got %g)", fn, sp.top_p);
-  const bool greedy = !(sp.temperature > 0.0);
-  const int k_eff = greedy ? 1 : ((sp.top_k > 0 && sp.top_k < V) ? sp.top_k : V);
-  if (k_eff > uno::kVerifyKMaxFast && V > uno::kVerifyCandCap)
-    return fail(UNO_ERR_UNSUPPORTED,
-                "%s: top-k %d (effective %d) over V = %d needs the full-row path, which this "
-                "build does not provide (single-pass selection handles k <= %d, or V <= %d)",
-                fn, sp.top_k, k_eff, V, uno::kVerifyKMaxFast, uno::kVerifyCandCap);
   return UNO_OK;
 }
 

@@ -67,11 +67,6 @@ struct GemmArgs {
   void* ws;
 };
 
-// Largest top-k the single-pass selection handles, and largest vocabulary that
-// may be taken whole when top-k is off.
-constexpr int kVerifyKMaxFast = 256;
-constexpr int kVerifyCandCap = 2048;
-
 size_t verify_workspace_bytes(int S, int b);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_draft(const DraftArgs& a, hipStream_t stream);

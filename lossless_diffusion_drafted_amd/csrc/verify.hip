@@ -40,7 +40,7 @@ constexpr int UNR = 8;                // 16-byte loads per thread per tile
 constexpr int CAND_CAP = 1024;        // candidates kept per row
 constexpr int WAVE_SEL_MAX = 512;     // candidates one wave selects from (8 per lane)
 constexpr int SEL_CAP = 256;          // largest filtered support on this path
-constexpr int KMAX_FAST = kVerifyKMaxFast;
+constexpr int KMAX_FAST = 256;          // largest top-k the stream bound is built for
 constexpr double NEAR_TIE = 1e-6;
 constexpr int PER_TILE = VT * UNR;    // 16-byte chunks per tile
 
@@ -767,6 +767,467 @@ __device__ __forceinline__ SlotResult decide_m(const Dist& dp, const Dist& dq, i
 }
 
 // --- kernels -------------------------------------------------------------------
+// ================================================================================
+// Full-row path: used when the settings make the filtered support large (top-k
+// off or k > KMAX_SINGLE_PASS over more than SEL_CAP logits) and as the fallback
+// of a slot whose single-pass selection overflows. The workgroup streams the whole
+// row several times (from L2 after the first pass) and never holds the support:
+//  * pass 1: row maximum (lowest id at it) and the top digit histogram of the
+//    order-preserving keys; further count passes give the exact tie-inclusive
+//    k-th largest key (MSB-first radix select, 8 bits per pass);
+//  * mass passes: the tie-grouped top-p cutoff by the same MSB-first search on
+//    histograms of softmax mass (the mass strictly above a bucket decides whether
+//    it is kept; the bucket where the running mass reaches top_p is refined).
+//    Masses are summed as 2^-40 fixed-point integers, so the order of the LDS
+//    atomics cannot change the result;
+//  * the decision needs p~(d) and q~(d) (one element each) and, on a rejection or
+//    at slot 0, one sum pass and one ordered scan pass over the residual or p~
+//    (inverse CDF in ascending id order, fp64 block scans).
+// ================================================================================
+constexpr int KMAX_SINGLE_PASS = 128;      // larger top-k goes to the full-row path
+constexpr double FIXED_ONE = 1099511627776.0;   // 2^40
+
+struct FullLds {
+  unsigned long long hm[256];   // fixed-point mass per digit
+  unsigned hc[256];             // element count per digit
+  double dred[VW];
+  float fred[VW];
+  int ired[VW];
+  unsigned uv[4];
+  unsigned long long qv[4];
+  double dv[4];
+  int tok;
+};
+
+struct RowSum {
+  float m;            // row maximum
+  int argmax;         // lowest id at the maximum
+  unsigned tau;       // kept iff the element's key >= tau (row key space)
+  double Zt;          // kept mass, sum over kept of exp((z - m) / T) (fixed point rounded)
+  double gap;         // top-p near-tie gap (infinity if none)
+  float c2hi, c2lo;   // log2(e) / T split in two floats
+};
+
+template <typename E> struct KeyBits { static constexpr int value = 32; };
+template <> struct KeyBits<uint16_t> { static constexpr int value = 16; };
+
+// Order-preserving key in the row's key space (bf16 rows need only the top 16 bits).
+template <typename E>
+__device__ __forceinline__ unsigned row_key(float x) {
+  return float_key(x) >> (32 - KeyBits<E>::value);
+}
+
+// exp((z - m) / T) in fp32 with the scaling done in two parts (the fp32 rounding
+// of log2(e)/T would otherwise scale every exponent).
+__device__ __forceinline__ float mass32(float z, const RowSum& rs) {
+  const float d = z - rs.m;
+  return __builtin_amdgcn_exp2f(fmaf(d, rs.c2hi, d * rs.c2lo));
+}
+
+__device__ __forceinline__ unsigned long long to_fixed(float w) {
+  return (unsigned long long)(double(w) * FIXED_ONE + 0.5);
+}
+
+// One 16-byte chunk of a row (values past the row read as zeros on the vector
+// path and as -inf on the scalar path; callers mask by index).
+template <typename E, bool VEC>
+__device__ __forceinline__ uint4 load_chunk(const RowView<E, VEC>& rv, int c) {
+  if constexpr (VEC) return buffer_load16(rv.rsrc, uint32_t(c) * 16u, 0u);
+  else return c < rv.nchunks ? Elem<E>::load_partial(rv.row, c * Elem<E>::VN, rv.V) : Elem<E>::neg_inf();
+}
+
+// Calls f(c, xp, xq) once per 16-byte chunk c of the rows (every thread; chunks
+// ascend across the workgroup in groups of VT; values past the row are -inf).
+// FULL_UNR chunks per row are in flight. f returns true to stop early (uniform
+// across the workgroup).
+constexpr int FULL_UNR = 4;
+template <typename E, bool VEC, typename F>
+__device__ __forceinline__ void stream_rows(const RowView<E, VEC>& pv, const RowView<E, VEC>& qv, bool two, F f) {
+  using EL = Elem<E>;
+  constexpr int VN = EL::VN;
+  const int ngroups = (pv.nchunks + VT - 1) / VT;
+  for (int g0 = 0; g0 < ngroups; g0 += FULL_UNR) {
+    uint4 rp[FULL_UNR], rq[FULL_UNR];
+#pragma unroll
+    for (int u = 0; u < FULL_UNR; ++u) {
+      const int c = (g0 + u) * VT + int(threadIdx.x);
+      rp[u] = load_chunk(pv, c);
+      if (two) rq[u] = load_chunk(qv, c);
+    }
+#pragma unroll
+    for (int u = 0; u < FULL_UNR; ++u) {
+      if (g0 + u >= ngroups) break;
+      const int c = (g0 + u) * VT + int(threadIdx.x);
+      float xp[VN], xq[VN];
+      EL::unpack(rp[u], xp);
+      if (two) EL::unpack(rq[u], xq);
+#pragma unroll
+      for (int j = 0; j < VN; ++j) {
+        if (c * VN + j >= pv.V) { xp[j] = -INFINITY; xq[j] = -INFINITY; }
+        if (!two) xq[j] = -INFINITY;
+      }
+      if (f(c, xp, xq)) return;
+    }
+  }
+}
+
+__device__ __forceinline__ double block_sum_d(double v, FullLds& fs) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) fs.dred[wid] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int w = 0; w < VW; ++w) t += fs.dred[w];
+  return t;
+}
+
+// Row summary (all threads return the same value).
+template <typename E, bool VEC>
+__device__ __forceinline__ RowSum summarize_row(const RowView<E, VEC>& rv, const FilterParams& fp, FullLds& fs) {
+  constexpr int KB = KeyBits<E>::value;
+  constexpr int LEVELS = KB / 8;
+  constexpr int VN = Elem<E>::VN;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int V = rv.V;
+  const bool kon = fp.k_eff < V;
+  RowSum rs;
+  const double c2 = 1.4426950408889634 / fp.T;
+  rs.c2hi = float(c2);
+  rs.c2lo = float(c2 - double(rs.c2hi));
+  rs.gap = INFINITY;
+
+  // pass 1: maximum, lowest id at it, top-digit counts
+  fs.hc[tid] = 0u;
+  __syncthreads();
+  float lm = -INFINITY;
+  int li = 0x7fffffff;
+  stream_rows(rv, rv, false, [&](int c, const float (&x)[VN], const float (&)[VN]) {
+#pragma unroll
+    for (int j = 0; j < VN; ++j) {
+      const int e = c * VN + j;
+      if (e < V) {
+        if (x[j] > lm || (x[j] == lm && e < li)) { lm = x[j]; li = e; }
+        if (kon) atomicAdd(&fs.hc[row_key<E>(x[j]) >> (KB - 8)], 1u);
+      }
+    }
+    return false;
+  });
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(lm, o, kWave);
+    const int oi = __shfl_xor(li, o, kWave);
+    if (om > lm || (om == lm && oi < li)) { lm = om; li = oi; }
+  }
+  if (lane == 0) { fs.fred[wid] = lm; fs.ired[wid] = li; }
+  __syncthreads();
+  lm = fs.fred[0];
+  li = fs.ired[0];
+#pragma unroll
+  for (int w = 1; w < VW; ++w)
+    if (fs.fred[w] > lm || (fs.fred[w] == lm && fs.ired[w] < li)) { lm = fs.fred[w]; li = fs.ired[w]; }
+  rs.m = lm;
+  rs.argmax = li;
+  if (fp.greedy) {
+    rs.tau = row_key<E>(lm);
+    rs.Zt = FIXED_ONE;
+    return rs;
+  }
+
+  // exact tie-inclusive k-th largest key
+  unsigned kth = 0u;
+  if (kon) {
+    unsigned prefix = 0u, remaining = unsigned(fp.k_eff);
+    for (int level = 0; level < LEVELS; ++level) {
+      const int shift = KB - 8 * (level + 1);
+      if (level > 0) {
+        __syncthreads();
+        fs.hc[tid] = 0u;
+        __syncthreads();
+        const unsigned pre = prefix >> (shift + 8);
+        stream_rows(rv, rv, false, [&](int c, const float (&x)[VN], const float (&)[VN]) {
+#pragma unroll
+          for (int j = 0; j < VN; ++j) {
+            const unsigned key = row_key<E>(x[j]);
+            if (c * VN + j < V && (key >> (shift + 8)) == pre) atomicAdd(&fs.hc[(key >> shift) & 255u], 1u);
+          }
+          return false;
+        });
+      }
+      __syncthreads();
+      if (tid == 0) {
+        unsigned cum = 0u, digit = 0u;
+        for (int d = 255; d >= 0; --d) {
+          if (cum + fs.hc[d] >= remaining) { digit = unsigned(d); break; }
+          cum += fs.hc[d];
+        }
+        fs.uv[0] = prefix | (digit << shift);
+        fs.uv[1] = remaining - cum;
+      }
+      __syncthreads();
+      prefix = fs.uv[0];
+      remaining = fs.uv[1];
+    }
+    kth = prefix;
+  }
+
+  // mass passes: total mass of the top-k set, then the top-p cutoff
+  unsigned prefix = 0u;
+  unsigned long long above = 0ull, zk = 0ull, hcut = 0ull;
+  unsigned n_above = 0u, nk = 0u, ncut = 0u;
+  const int mlevels = fp.topp_on ? LEVELS : 1;
+  for (int level = 0; level < mlevels; ++level) {
+    const int shift = KB - 8 * (level + 1);
+    __syncthreads();
+    fs.hm[tid] = 0ull;
+    fs.hc[tid] = 0u;
+    __syncthreads();
+    const unsigned pre = level == 0 ? 0u : prefix >> (shift + 8);
+    stream_rows(rv, rv, false, [&](int c, const float (&x)[VN], const float (&)[VN]) {
+#pragma unroll
+      for (int j = 0; j < VN; ++j) {
+        const unsigned key = row_key<E>(x[j]);
+        if (c * VN + j < V && key >= kth && (level == 0 || (key >> (shift + 8)) == pre)) {
+          const unsigned dgt = (key >> shift) & 255u;
+          atomicAdd(&fs.hm[dgt], to_fixed(mass32(x[j], rs)));
+          atomicAdd(&fs.hc[dgt], 1u);
+        }
+      }
+      return false;
+    });
+    __syncthreads();
+    if (tid == 0) {
+      if (level == 0) {
+        unsigned long long t = 0ull;
+        unsigned n = 0u;
+        for (int d = 0; d < 256; ++d) { t += fs.hm[d]; n += fs.hc[d]; }
+        fs.qv[0] = t;
+        fs.uv[0] = n;
+      }
+      if (fp.topp_on) {
+        const double thr = fp.top_p * double(level == 0 ? fs.qv[0] : zk);
+        unsigned long long run = above;
+        unsigned nrun = n_above;
+        int cand = -1;
+        unsigned long long a_c = 0ull;
+        unsigned n_c = 0u;
+        for (int d = 255; d >= 0; --d) {
+          if (fs.hc[d] > 0u) {
+            if (double(run) < thr) { cand = d; a_c = run; n_c = nrun; }
+            else break;
+          }
+          run += fs.hm[d];
+          nrun += fs.hc[d];
+        }
+        if (cand < 0) cand = 0;                  // unreachable: the top bucket always qualifies
+        fs.uv[1] = prefix | (unsigned(cand) << shift);
+        fs.qv[1] = a_c;
+        fs.uv[2] = n_c;
+        fs.qv[2] = fs.hm[cand];
+        fs.uv[3] = fs.hc[cand];
+      }
+    }
+    __syncthreads();
+    if (level == 0) { zk = fs.qv[0]; nk = fs.uv[0]; }
+    if (fp.topp_on) {
+      prefix = fs.uv[1];
+      above = fs.qv[1];
+      n_above = fs.uv[2];
+      hcut = fs.qv[2];
+      ncut = fs.uv[3];
+    }
+  }
+  if (fp.topp_on) {
+    rs.tau = prefix;
+    rs.Zt = double(above + hcut);
+    const double Zk = double(zk);
+    if (above > 0ull) rs.gap = fabs(double(above) / Zk - fp.top_p);
+    if (n_above + ncut < nk) rs.gap = fmin(rs.gap, fabs(double(above + hcut) / Zk - fp.top_p));
+  } else {
+    rs.tau = kth;
+    rs.Zt = double(zk);
+  }
+  return rs;
+}
+
+// Filtered probability of one element from its logit (fp64 weight).
+template <typename E>
+__device__ __forceinline__ double full_prob(const RowSum& rs, const FilterParams& fp, float z, int id) {
+  if (fp.greedy) return id == rs.argmax ? 1.0 : 0.0;
+  if (!(row_key<E>(z) >= rs.tau) || !(z > -INFINITY)) return 0.0;
+  return exp((double(z) - double(rs.m)) / fp.T) * FIXED_ONE / rs.Zt;
+}
+
+// Per-element weight in the scan passes (fp32 mass, consistent with Zt).
+template <typename E>
+__device__ __forceinline__ double full_weight(const RowSum& rs, const FilterParams& fp, float z, int id) {
+  if (fp.greedy) return id == rs.argmax ? 1.0 : 0.0;
+  if (!(row_key<E>(z) >= rs.tau) || !(z > -INFINITY)) return 0.0;
+  return double(to_fixed(mass32(z, rs))) / rs.Zt;
+}
+
+template <typename E, bool VEC>
+__device__ __forceinline__ float load_elem(const RowView<E, VEC>& rv, int e) {
+  if constexpr (sizeof(E) == 2) return bf16_to_f32(rv.row[e]);
+  else return rv.row[e];
+}
+
+// Weight of element e of the residual (mode 1: max(0, p~ - q~)) or of p~ / q~ alone
+// (mode 0: the first row's filtered distribution).
+template <typename E>
+__device__ __forceinline__ double scan_weight(int mode, const RowSum& r1, const RowSum& r2, const FilterParams& fp,
+                                              float x1, float x2, int e) {
+  const double a = full_weight<E>(r1, fp, x1, e);
+  if (mode == 0) return a;
+  return fmax(0.0, a - full_weight<E>(r2, fp, x2, e));
+}
+
+// Inverse CDF over ascending ids: the first e whose running weight sum exceeds
+// u * W (W = total weight). Sets *tie when u*W lies within 1e-6*W of a boundary
+// next to the drawn element, and *wsum to W.
+template <typename E, bool VEC>
+__device__ __forceinline__ int full_icdf(const RowView<E, VEC>& v1, const RowView<E, VEC>& v2, int mode, const RowSum& r1,
+                         const RowSum& r2, const FilterParams& fp, double u, FullLds& fs, bool* tie, double* wsum) {
+  constexpr int VN = Elem<E>::VN;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const bool two = mode == 1;
+  // total weight, positive-weight count and the last positive id
+  double lw = 0.0;
+  int lastpos = -1;
+  stream_rows(v1, v2, two, [&](int c, const float (&x1)[VN], const float (&x2)[VN]) {
+#pragma unroll
+    for (int j = 0; j < VN; ++j) {
+      const int e = c * VN + j;
+      if (e < v1.V) {
+        const double w = scan_weight<E>(mode, r1, r2, fp, x1[j], x2[j], e);
+        lw += w;
+        if (w > 0.0) lastpos = e;
+      }
+    }
+    return false;
+  });
+  const double W = block_sum_d(lw, fs);
+  lastpos = wave_max(lastpos);
+  __syncthreads();
+  if (lane == 0) fs.ired[wid] = lastpos;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < VW; ++w) lastpos = max(lastpos, fs.ired[w]);
+  *wsum = W;
+  const double t = u * W;
+  if (tid == 0) { fs.tok = -1; fs.dv[0] = 0.0; fs.dv[1] = 0.0; }
+  __syncthreads();
+  double run = 0.0;                            // sum of all earlier sub-tiles (same in every thread)
+  stream_rows(v1, v2, two, [&](int c, const float (&x1)[VN], const float (&x2)[VN]) {
+    double w[VN];
+    double ls = 0.0;
+#pragma unroll
+    for (int j = 0; j < VN; ++j) {
+      const int e = c * VN + j;
+      w[j] = e < v1.V ? scan_weight<E>(mode, r1, r2, fp, x1[j], x2[j], e) : 0.0;
+      ls += w[j];
+    }
+    // block inclusive scan of the chunk sums; the crossing chunk is the lowest
+    // thread whose inclusive bound exceeds t (unique even under rounding)
+    const double incl = wave_inclusive_scan(ls);
+    __syncthreads();
+    if (lane == kWave - 1) fs.dred[wid] = incl;
+    if (tid == 0) fs.ired[0] = 0x7fffffff;
+    __syncthreads();
+    double woff = 0.0, tot = 0.0;
+#pragma unroll
+    for (int q = 0; q < VW; ++q) {
+      if (q < wid) woff += fs.dred[q];
+      tot += fs.dred[q];
+    }
+    const double bound = run + woff + incl;
+    const double up = __shfl_up(bound, 1, kWave);
+    const double prev = lane > 0 ? up : run + woff;
+    if (bound > t) atomicMin(&fs.ired[0], tid);
+    __syncthreads();
+    if (tid == fs.ired[0]) {
+      double cum = prev;
+      int pick = -1, lastp = -1;
+      double lo = prev, hi = prev;
+#pragma unroll
+      for (int j = 0; j < VN; ++j) {
+        const double nxt = cum + w[j];
+        if (w[j] > 0.0) {
+          lastp = j;
+          if (pick < 0 && nxt > t) { pick = j; lo = cum; hi = nxt; }
+        }
+        cum = nxt;
+      }
+      if (pick < 0) { pick = lastp < 0 ? 0 : lastp; lo = prev; hi = bound; }
+      fs.tok = c * VN + pick;
+      fs.dv[0] = lo;
+      fs.dv[1] = hi;
+    }
+    __syncthreads();
+    run += tot;
+    return fs.tok >= 0;
+  });
+  __syncthreads();
+  int tok = fs.tok;
+  bool tnear = false;
+  if (tok < 0) {
+    tok = max(lastpos, 0);                     // rounding left u*W at the very end
+  } else {
+    const double lo = fs.dv[0], hi = fs.dv[1];
+    if (lo > 0.0 && fabs(t - lo) < NEAR_TIE * W) tnear = true;
+    if (tok != lastpos && fabs(hi - t) < NEAR_TIE * W) tnear = true;
+  }
+  *tie = tnear;
+  return tok;
+}
+
+// One slot by the full-row path (all threads of the workgroup). For a draft-only
+// call pass has_q = false with the draft row as `pv` and the draw in u_res.
+template <typename E, bool VEC>
+__device__ __forceinline__ SlotResult full_slot(const RowView<E, VEC>& pv, const RowView<E, VEC>& qv, bool has_q,
+                                const FilterParams& fp, int d, double u_acc, double u_res, FullLds& fs,
+                                int* topp_flags) {
+  SlotResult res;
+  res.flags = 0;
+  res.ratio = 1.0;
+  const RowSum rp = summarize_row(pv, fp, fs);
+  *topp_flags = rp.gap < NEAR_TIE ? FLAG_TIE_TOPP_P : 0;
+  bool tie = false;
+  double W = 0.0;
+  if (!has_q) {
+    res.acc = 1;
+    res.tok = full_icdf(pv, pv, 0, rp, rp, fp, u_res, fs, &tie, &W);
+    if (tie) res.flags |= FLAG_TIE_ICDF;
+    return res;
+  }
+  const RowSum rq = summarize_row(qv, fp, fs);
+  if (rq.gap < NEAR_TIE) *topp_flags |= FLAG_TIE_TOPP_Q;
+  const bool din = d >= 0 && d < pv.V;
+  const double pd = din ? full_prob<E>(rp, fp, load_elem(pv, d), d) : 0.0;
+  const double qd = din ? full_prob<E>(rq, fp, load_elem(qv, d), d) : 0.0;
+  if (qd == 0.0) {
+    res.acc = 0;
+    res.ratio = 0.0;
+    res.flags |= FLAG_Q_ZERO;
+  } else {
+    res.ratio = pd / qd;
+    res.acc = u_acc < res.ratio ? 1 : 0;
+    if (fabs(u_acc - res.ratio) < NEAR_TIE) res.flags |= FLAG_TIE_ACCEPT;
+  }
+  if (res.acc) {
+    res.tok = d;
+    return res;
+  }
+  res.tok = full_icdf(pv, qv, 1, rp, rq, fp, u_res, fs, &tie, &W);
+  if (W == 0.0) {                               // zero residual: draw from p~
+    res.flags |= FLAG_RES_ZERO;
+    res.tok = full_icdf(pv, pv, 0, rp, rp, fp, u_res, fs, &tie, &W);
+  }
+  if (tie) res.flags |= FLAG_TIE_ICDF;
+  return res;
+}
+
 template <typename E, bool VEC>
 __global__ __launch_bounds__(VT) void verify_kernel(VerifyArgs a) {
   __shared__ Shared sh;
@@ -782,70 +1243,77 @@ __global__ __launch_bounds__(VT) void verify_kernel(VerifyArgs a) {
 
   const RowView<E, VEC> pv(static_cast<const E*>(a.p) + off, V);
   const RowView<E, VEC> qv(static_cast<const E*>(a.q) + off, V);
-  reset_row(Rp);
-  reset_row(Rq);
-  bool done = false;
-  if constexpr (VEC) {
-    if (has_q) {
-      stream_two<E>(pv, qv, fp, Rp, Rq, sh);
-      done = true;
+  // Settings whose filtered support can be large go straight to the full-row
+  // path; otherwise the single-pass path runs and falls back to the full-row path
+  // for a slot whose candidate list or top-k set overflows.
+  bool use_full = fp.k_eff > KMAX_SINGLE_PASS && V > SEL_CAP;
+  if (!use_full) {
+    reset_row(Rp);
+    reset_row(Rq);
+    bool done = false;
+    if constexpr (VEC) {
+      if (has_q) {
+        stream_two<E>(pv, qv, fp, Rp, Rq, sh);
+        done = true;
+      }
     }
-  }
-  if (!done) {
-    stream_one(pv, fp, Rp, sh);
-    if (has_q) stream_one(qv, fp, Rq, sh);
-  }
+    if (!done) {
+      stream_one(pv, fp, Rp, sh);
+      if (has_q) stream_one(qv, fp, Rq, sh);
+    }
 
-  // Selection: one wave per row when both candidate lists are small enough.
-  const int cp = Rp.cnt, cq = has_q ? Rq.cnt : 0;
-  __syncthreads();                  // every thread has read the counts
-  if (tid == 0) {
-    if (cp > CAND_CAP) Rp.status = ROW_OVERFLOW;
-    if (cq > CAND_CAP) Rq.status = ROW_OVERFLOW;
+    // Selection: one wave per row when both candidate lists are small enough.
+    const int cp = Rp.cnt, cq = has_q ? Rq.cnt : 0;
+    __syncthreads();                  // every thread has read the counts
+    if (tid == 0) {
+      if (cp > CAND_CAP) Rp.status = ROW_OVERFLOW;
+      if (cq > CAND_CAP) Rq.status = ROW_OVERFLOW;
+    }
+    __syncthreads();
+    if (cp <= WAVE_SEL_MAX && cq <= WAVE_SEL_MAX) {
+      if (wid == 0) wave_select(Rp, fp);
+      if (wid == 1 && has_q) wave_select(Rq, fp);
+    } else {
+      if (Rp.status == ROW_OK) block_select(Rp, fp, sh);
+      if (has_q && Rq.status == ROW_OK) block_select(Rq, fp, sh);
+    }
+    __syncthreads();
+    if (wid == 0 && Rp.status == ROW_OK) wave_filter(fp, Rp, sh.dist[0]);
+    if (wid == 1 && has_q && Rq.status == ROW_OK) wave_filter(fp, Rq, sh.dist[1]);
+    __syncthreads();
+    use_full = Rp.status != ROW_OK || (has_q && Rq.status != ROW_OK);
   }
-  __syncthreads();
-  if (cp <= WAVE_SEL_MAX && cq <= WAVE_SEL_MAX) {
-    if (wid == 0) wave_select(Rp, fp);
-    if (wid == 1 && has_q) wave_select(Rq, fp);
-  } else {
-    if (Rp.status == ROW_OK) block_select(Rp, fp, sh);
-    if (has_q && Rq.status == ROW_OK) block_select(Rq, fp, sh);
-  }
-  __syncthreads();
-  if (wid == 0 && Rp.status == ROW_OK) wave_filter(fp, Rp, sh.dist[0]);
-  if (wid == 1 && has_q && Rq.status == ROW_OK) wave_filter(fp, Rq, sh.dist[1]);
-  __syncthreads();
-
-  if (wid != 0) return;             // wave 0 finishes the slot alone
 
   const Philox4 ph = philox4x64_10(uint64_t(a.pos[s] + i), 0ull, 0ull, 0ull, a.sp.seed,
                                    uint64_t(a.seq_ids[s]));
   const double u_acc = word_to_uniform(ph.w[0]);
   const double u_res = word_to_uniform(ph.w[1]);
-  const Dist& dp = sh.dist[0];
-  const Dist& dq = sh.dist[1];
   SlotResult res;
-  res.tok = -1;
-  res.acc = 0;
-  res.flags = 0;
-  res.ratio = 1.0;
-  const bool ok_p = Rp.status == ROW_OK;
-  const bool ok_q = !has_q || Rq.status == ROW_OK;
-  if (!ok_p || !ok_q) {
-    res.acc = has_q ? 0 : 1;
-    res.flags |= FLAG_OVERFLOW;
-  } else if (!has_q) {
-    res.acc = 1;
-    bool tie = false;
-    res.tok = sample_dist(dp, u_res, &tie);
-    if (tie) res.flags |= FLAG_TIE_ICDF;
+  if (use_full) {
+    __shared__ FullLds fsh;
+    int topp = 0;
+    res = full_slot(pv, qv, has_q, fp, has_q ? a.draft[g] : -1, u_acc, u_res, fsh, &topp);
+    res.flags |= topp;
+    if (wid != 0) return;
   } else {
-    const int d = a.draft[g];
-    res = dp.n <= kWave ? decide_m<1>(dp, dq, d, u_acc, u_res)
-                        : decide_m<SEL_CAP / kWave>(dp, dq, d, u_acc, u_res);
-    if (dq.gap < NEAR_TIE) res.flags |= FLAG_TIE_TOPP_Q;
+    if (wid != 0) return;             // wave 0 finishes the slot alone
+    const Dist& dp = sh.dist[0];
+    const Dist& dq = sh.dist[1];
+    if (!has_q) {
+      res.acc = 1;
+      res.flags = 0;
+      res.ratio = 1.0;
+      bool tie = false;
+      res.tok = sample_dist(dp, u_res, &tie);
+      if (tie) res.flags |= FLAG_TIE_ICDF;
+    } else {
+      const int d = a.draft[g];
+      res = dp.n <= kWave ? decide_m<1>(dp, dq, d, u_acc, u_res)
+                          : decide_m<SEL_CAP / kWave>(dp, dq, d, u_acc, u_res);
+      if (dq.gap < NEAR_TIE) res.flags |= FLAG_TIE_TOPP_Q;
+    }
+    if (dp.gap < NEAR_TIE) res.flags |= FLAG_TIE_TOPP_P;
   }
-  if (ok_p && dp.gap < NEAR_TIE) res.flags |= FLAG_TIE_TOPP_P;
 
   // Slot record, then the per-sequence ticket.
   unsigned* counters = static_cast<unsigned*>(a.ws);
@@ -898,30 +1366,41 @@ __global__ __launch_bounds__(VT) void draft_kernel(DraftArgs a) {
   const FilterParams fp = make_filter_params(a.sp, V);
   RowLds& R = sh.row[1];
   const RowView<E, VEC> qv(static_cast<const E*>(a.q) + size_t(g) * V, V);
-  reset_row(R);
-  stream_one(qv, fp, R, sh);
-  const int c = R.cnt;
-  __syncthreads();
-  if (c > CAND_CAP && tid == 0) R.status = ROW_OVERFLOW;
-  __syncthreads();
-  if (c <= WAVE_SEL_MAX) {
-    if (wid == 0) wave_select(R, fp);
-  } else if (R.status == ROW_OK) {
-    block_select(R, fp, sh);
+  const Philox4 ph = philox4x64_10(uint64_t(a.pos[s] + i), 1ull, 0ull, 0ull, a.sp.seed,
+                                   uint64_t(a.seq_ids[s]));
+  const double u = word_to_uniform(ph.w[0]);
+  bool use_full = fp.k_eff > KMAX_SINGLE_PASS && V > SEL_CAP;
+  if (!use_full) {
+    reset_row(R);
+    stream_one(qv, fp, R, sh);
+    const int c = R.cnt;
+    __syncthreads();
+    if (c > CAND_CAP && tid == 0) R.status = ROW_OVERFLOW;
+    __syncthreads();
+    if (c <= WAVE_SEL_MAX) {
+      if (wid == 0) wave_select(R, fp);
+    } else if (R.status == ROW_OK) {
+      block_select(R, fp, sh);
+    }
+    __syncthreads();
+    use_full = R.status != ROW_OK;
   }
-  __syncthreads();
-  if (wid != 0) return;
   int flags = 0, tok = -1;
-  if (R.status == ROW_OK) {
+  if (use_full) {
+    // the draft row's filtered distribution, drawn like an AR slot
+    __shared__ FullLds fsh;
+    int topp = 0;
+    const SlotResult r = full_slot(qv, qv, false, fp, -1, 0.0, u, fsh, &topp);
+    tok = r.tok;
+    flags = (r.flags & FLAG_TIE_ICDF) | ((topp & FLAG_TIE_TOPP_P) ? FLAG_TIE_TOPP_Q : 0);
+    if (wid != 0) return;
+  } else {
+    if (wid != 0) return;
     wave_filter(fp, R, sh.dist[1]);
-    const Philox4 ph = philox4x64_10(uint64_t(a.pos[s] + i), 1ull, 0ull, 0ull, a.sp.seed,
-                                     uint64_t(a.seq_ids[s]));
     bool tie = false;
-    tok = sample_dist(sh.dist[1], word_to_uniform(ph.w[0]), &tie);
+    tok = sample_dist(sh.dist[1], u, &tie);
     if (tie) flags |= FLAG_TIE_ICDF;
     if (sh.dist[1].gap < NEAR_TIE) flags |= FLAG_TIE_TOPP_Q;
-  } else {
-    flags |= FLAG_OVERFLOW;
   }
   if (tid == 0) {
     a.draft[g] = tok;

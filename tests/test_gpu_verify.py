@@ -87,19 +87,12 @@ def test_verify_qwen_distribution_reduced(V, S, b, seed):
     assert st["exact"] >= S - 1
 
 
-# Settings whose filtered support (top-k off over more than 256 logits) or
-# candidate list (k near 256 over a few thousand logits) outgrows the single-pass
-# selection: the full-row path that handles them is not built yet, and the slots
-# are flagged UNO_FLAG_OVERFLOW instead.
-_FULL_ROW = pytest.mark.skip(reason="needs the full-row verify path (not built yet); such slots are flagged")
-
-
 @pytest.mark.parametrize("V,b,k,top_p,T", [
     (1, 4, 50, 0.95, 1.0), (7, 3, 50, 0.95, 1.0), (50, 8, 50, 0.95, 1.0), (51, 8, 50, 0.9, 1.0),
     (1000, 1, 50, 0.95, 1.0), (4099, 5, 50, 0.95, 1.0), (2051, 64, 50, 0.5, 0.7),
-    pytest.param(300, 6, 0, 1.0, 1.0, marks=_FULL_ROW), pytest.param(2048, 4, 0, 0.95, 1.3, marks=_FULL_ROW),
+    (300, 6, 0, 1.0, 1.0), (2048, 4, 0, 0.95, 1.3),              # top-k off: full-row path
     (3000, 4, 1, 0.95, 1.0), (3000, 4, 50, 1e-9, 1.0),
-    pytest.param(3000, 6, 256, 0.99, 2.0, marks=_FULL_ROW), pytest.param(3000, 6, 200, 0.99, 2.0, marks=_FULL_ROW),
+    (3000, 6, 256, 0.99, 2.0), (3000, 6, 200, 0.99, 2.0), (3000, 6, 128, 0.9, 1.0),
     (5000, 6, 50, 0.95, 0.0),
     (40000, 3, 50, 0.95, 1.0), (70001, 2, 7, 0.9, 0.8),
 ])
@@ -196,31 +189,60 @@ def test_repeat_runs_are_identical():
         assert torch.equal(cur, first)
 
 
-@pytest.mark.parametrize("V,k", [(2049, 0), (5000, 0), (5000, 1000)])
-def test_full_row_settings_are_refused_up_front(V, k):
-    """Top-k off or k > 256 over more than 2048 logits needs a full-row path this
-    build does not provide: the call must fail before launching anything."""
-    uno = _uno()
-    cfg = dict(workloads.VERIFY_CONFIGS["qwen"], S=2, b=3)
-    p, q = workloads.verify_logits(cfg, seed=1, V=V)
-    seq, pos = np.arange(2, dtype=np.int64), np.zeros(2, dtype=np.int64)
-    with pytest.raises(uno.UnoError) as e:
-        uno.uno_verify_block(to_device(p, DEV), to_device(q, DEV),
-                             to_device(np.zeros((2, 3), np.int32), DEV), to_device(seq, DEV),
-                             to_device(pos, DEV), top_k=k)
-    assert e.value.status == "UNO_ERR_UNSUPPORTED"
+@pytest.mark.parametrize("V,b,k,top_p,T,dtype", [
+    (40000, 4, 0, 0.95, 1.0, "bf16"),      # top-k off over a large vocabulary
+    (40000, 4, 0, 1.0, 1.0, "bf16"),       # no filter at all
+    (20000, 3, 1000, 0.9, 0.8, "bf16"),    # large top-k
+    (20000, 3, 300, 1.0, 1.2, "f32"),      # large top-k, fp32 keys (four radix levels)
+    (20001, 3, 0, 0.5, 1.0, "f32"),        # rows not 16-byte aligned
+])
+def test_verify_full_row_path(V, b, k, top_p, T, dtype):
+    """Settings whose filtered support is large take the multi-pass full-row path;
+    its tokens must agree with the oracle exactly outside near-ties."""
+    S = 3
+    cfg = dict(workloads.VERIFY_CONFIGS["qwen"], S=S, b=b, dtype=dtype)
+    p, q = workloads.verify_logits(cfg, seed=V + k, V=V)
+    sp = dict(temperature=T, top_k=k, top_p=top_p, seed=5)
+    st, gpu, ref = _run_full(p, q, sp)
+    print(V, b, k, top_p, T, dtype, st)
+    assert st["exact"] + st["near_tie"] == S and st["exact"] >= S - 1
 
 
-def test_massive_ties_are_flagged_not_wrong():
-    """A row of identical logits keeps the whole vocabulary in its tie-inclusive
-    top-k set: beyond this path's capacity the slot is flagged, never mis-sampled."""
+@pytest.mark.parametrize("V,k,top_p", [(40000, 0, 0.95), (20000, 500, 1.0)])
+def test_draft_sampler_full_row_path(V, k, top_p):
     uno = _uno()
-    S, b, V = 1, 2, 5000
-    z = np.zeros((S, b, V), np.float32)
+    cfg = dict(workloads.VERIFY_CONFIGS["qwen"], S=4, b=4)
+    _, q = workloads.verify_logits(cfg, seed=V, V=V)
+    S = q.shape[0]
     seq, pos = np.arange(S, dtype=np.int64), np.zeros(S, dtype=np.int64)
-    r = uno.uno_verify_block(to_device(z, DEV), to_device(z, DEV), to_device(np.zeros((S, b), np.int32), DEV),
-                             to_device(seq, DEV), to_device(pos, DEV))
+    sp = dict(temperature=1.0, top_k=k, top_p=top_p, seed=3)
+    ref, rflags = oracle.draft_sample(q, seq, pos, sp["temperature"], sp["top_k"], sp["top_p"], sp["seed"], "bf16")
+    d, flags = uno.uno_draft_sample(to_device(q, DEV), to_device(seq, DEV), to_device(pos, DEV), **sp)
     torch.cuda.synchronize()
-    flags = r["diag"][..., 3].cpu().numpy().astype(np.int64)
-    assert np.all(flags & 64)
-    assert np.all(r["out_tokens"].cpu().numpy()[:, 1:] == -1)
+    d, flags = d.cpu().numpy(), flags.cpu().numpy()
+    tie = (flags | rflags) & oracle.TIE_MASK
+    np.testing.assert_array_equal(d[tie == 0], ref[tie == 0])
+    assert np.count_nonzero(tie) <= 1
+
+
+def test_massive_ties_take_the_full_row_path():
+    """A row of identical logits keeps the whole vocabulary in its tie-inclusive
+    top-k set, far beyond the single pass's capacity: the slot falls back to the
+    full-row path and matches the oracle (uniform distribution, every draft kept)."""
+    S, b, V = 2, 3, 5000
+    z = np.zeros((S, b, V), np.float32)
+    z[1, :, 17] = 1.0                                     # one sequence with a unique maximum
+    st, gpu, ref = _run_full(z, z.copy(), SP)
+    assert not np.any(gpu["diag"][..., 3].astype(np.int64) & 64)
+    assert st["exact"] + st["near_tie"] == S
+
+
+def test_greedy_ties_take_the_lowest_id():
+    """T = 0 with a maximum shared by more tokens than the single pass holds: the
+    lowest id wins (through the full-row fallback)."""
+    S, b, V = 1, 4, 3000
+    z = np.zeros((S, b, V), np.float32)
+    z[..., 500:] = 2.0                                    # 2500 tokens tie at the maximum
+    st, gpu, ref = _run_full(z, z.copy(), dict(SP, temperature=0.0))
+    assert st["exact"] == S
+    assert gpu["out_tokens"][0, 0] == 500
