@@ -84,7 +84,8 @@ int uno_abi_version(void);
 
 /* Fill `bytes` of device memory with zeros on `stream` (a fill kernel, safe to
  * record in a HIP graph). Every workspace must be zeroed once before its first
- * use; each call leaves it zeroed again for the next call. */
+ * use; each call leaves it valid for the next call (it may carry state from one
+ * call to the next), so the caller never writes to it afterwards. */
 int uno_workspace_init(void* workspace, size_t bytes, void* stream);
 
 /* ---------------------------------------------------------------------------

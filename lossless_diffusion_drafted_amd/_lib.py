@@ -142,8 +142,8 @@ def require(t, name, dtype=None, shape=None, device=None):
 class Workspaces:
     """Zero-initialised device workspaces, one per (device, stream, purpose).
 
-    Each library call leaves its workspace zeroed again, so a buffer is cleared only
-    when it is first allocated or grown."""
+    Each library call leaves its workspace valid for the next call, so a buffer is
+    cleared only when it is first allocated or grown."""
 
     def __init__(self):
         self._bufs = {}

@@ -20,9 +20,11 @@
 //   barrier. Pass 2: p, q from the stored exps, sum |q - p| and sum q sign(q - p);
 //   the registers now hold (sign, q). Second barrier. Pass 3: the gradient,
 //   rounded to bf16 by the hardware conversion, written with streaming stores.
-// * Team barriers are counters in the workspace with bounded spins; a spin that
-//   runs out sets an abort flag that every waiter polls, so every wait ends (the
-//   loss is then NaN).
+// * Team exchanges are tagged record words in the workspace: each member stores
+//   its partials with a tag (call epoch, barrier number) and polls the other
+//   members' words until their tags match, so no wait drains the gradient
+//   stores in flight. Polls are bounded; one that runs out sets an abort flag
+//   that every poller checks, so every wait ends (the loss is then NaN).
 
 #include "../../include/uno.h"
 #include "common.h"
@@ -47,20 +49,21 @@ struct TvPlan {
   int xcd;        // 1: team members share an XCD (grid is a multiple of 8 G)
 };
 
-// Workspace: [header | team counters (64 B each) | team records (64 B per
-// workgroup) | per-row TV (double)].
+// Workspace: [header | team records (8 words of 64 bits per workgroup) | per-row
+// TV (double)]. A record word holds an fp32 value in its low half and a tag in
+// its high half: (call epoch << 16) | barrier number.
 struct TvHeader {
   unsigned done;
   unsigned abort;
   unsigned nresp;
+  unsigned epoch;      // calls completed (mod 2^16 in tags)
 };
-constexpr size_t kCtrOff = 256;
-constexpr size_t kRecOff = kCtrOff + size_t(kMaxWg) * 64;
+constexpr size_t kRecOff = 256;
 constexpr size_t kRowOff = kRecOff + size_t(kMaxWg) * 64;
 
 struct TvLds {
   float wred[TWAVES][4];
-  double rec[64][4];
+  float rec[64][4];
   float norm[4];
   int ok;
   int last;
@@ -193,17 +196,58 @@ __device__ __forceinline__ void store_grad(E* row, int V, int c0, const float (&
   }
 }
 
-// Team barrier: thread 0 has published this workgroup's record; count the
-// arrival and wait until all G members of barrier number `n` have arrived.
-__device__ bool team_barrier(unsigned* ctr, unsigned target, unsigned* abort_flag, TvLds& sh) {
-  if (threadIdx.x == 0) {
-    // The record was written with device-coherent stores; the wait retires them
-    // before the arrival is counted.
-    __builtin_amdgcn_s_waitcnt(0);
-    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bool ok = true;
+// Next-row prefetch (bf16 rows on the vector path): the workgroup's slices of
+// the next response row are copied into LDS by buffer loads that write LDS
+// directly, while the current row is computed and exchanged. Thread t's chunk u
+// of tensor x lands at pre[x][u][t].
+template <typename E, bool VEC> struct TvPrefetch { static constexpr bool on = false; };
+template <> struct TvPrefetch<uint16_t, true> { static constexpr bool on = false; };
+constexpr int PRE_CH = EPT / 8;          // 16-byte chunks per thread per tensor (bf16)
+
+__device__ __forceinline__ void prefetch_row(const uint16_t* trow, const uint16_t* srow, int V, int c0,
+                                             uint4* pre) {
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  const __amdgpu_buffer_rsrc_t rt = slice_rsrc(trow, V, c0, 2), rs = slice_rsrc(srow, V, c0, 2);
+#pragma unroll
+  for (int u = 0; u < PRE_CH; ++u) {
+    const uint32_t off = uint32_t((u * TT + int(threadIdx.x)) * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (__attribute__((address_space(3))) void*)(pre + u * TT + wave * kWave),
+                                             16, off, 0, 0, kBufNonTemporal);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(pre + (PRE_CH + u) * TT + wave * kWave),
+                                             16, off, 0, 0, kBufNonTemporal);
+  }
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void tv_wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Team exchange without a counter: each member publishes its n partials as
+// tagged words (64-bit device-coherent stores, no wait), and every member polls
+// the team's words until all carry the current tag. Nothing older than the
+// record (gradient stores, LDS prefetches) has to retire first. Polls are bounded:
+// a poll that runs out raises the abort flag, which every poller checks, so every
+// wait ends.
+__device__ __forceinline__ void publish(unsigned long long* rec, const float* v, int n, unsigned tag) {
+  for (int k = 0; k < n; ++k)
+    __hip_atomic_store(&rec[k], ((unsigned long long)tag << 32) | __float_as_uint(v[k]), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ bool gather(const unsigned long long* team_rec, int G, int slot, int n, unsigned tag,
+                       unsigned* abort_flag, TvLds& sh) {
+  const int tid = threadIdx.x;
+  if (tid < G * n) {
+    const int j = tid / n, k = tid - j * n;
+    const unsigned long long* w = &team_rec[j * 8 + slot * 4 + k];
     unsigned spins = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    unsigned long long v = 0ull;
+    bool ok = true;
+    while (true) {
+      v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (unsigned(v >> 32) == tag) break;
       if ((++spins & 63u) == 0u) {
         if (__hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) { ok = false; break; }
         if (spins > kSpinLimit) {
@@ -212,30 +256,13 @@ __device__ bool team_barrier(unsigned* ctr, unsigned target, unsigned* abort_fla
           break;
         }
       }
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(1);
     }
-    sh.ok = ok ? 1 : 0;
+    sh.rec[j][k] = __uint_as_float(unsigned(v));
+    if (!ok) sh.ok = 0;
   }
   __syncthreads();
   return sh.ok != 0;
-}
-
-__device__ __forceinline__ void put_record(double* rec, double a, double b, double c, double d) {
-  __hip_atomic_store(&rec[0], a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(&rec[1], b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(&rec[2], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(&rec[3], d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// The G records of the team (4 doubles each) into LDS.
-__device__ __forceinline__ void get_records(const double* team_rec, int G, int slot, TvLds& sh) {
-  const int tid = threadIdx.x;
-  if (tid < 4 * G) {
-    const int j = tid >> 2, k = tid & 3;
-    sh.rec[j][k] = __hip_atomic_load(&team_rec[j * 8 + slot * 4 + k], __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
 }
 
 template <typename E, bool VEC>
@@ -254,9 +281,11 @@ __global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
   }
   char* ws = static_cast<char*>(a.ws);
   TvHeader* hdr = reinterpret_cast<TvHeader*>(ws);
-  unsigned* ctr = reinterpret_cast<unsigned*>(ws + kCtrOff + size_t(team) * 64);
-  double* team_rec = reinterpret_cast<double*>(ws + kRecOff + size_t(team) * G * 64);
-  double* my_rec = team_rec + member * 8;
+  unsigned long long* team_rec = reinterpret_cast<unsigned long long*>(ws + kRecOff + size_t(team) * G * 64);
+  unsigned long long* my_rec = team_rec + member * 8;
+  const unsigned epoch_tag =
+      (__hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xffffu) << 16;
+  if (tid == 0) sh.ok = 1;
   double* row_tv = reinterpret_cast<double*>(ws + kRowOff);
 
   const int V = a.V;
@@ -269,21 +298,64 @@ __global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
   E* gbase = static_cast<E*>(a.grad);
   unsigned nbar = 0;
   bool ok = true;
+  constexpr bool PRE = TvPrefetch<E, VEC>::on;
+  __shared__ uint4 pre[PRE ? 2 * PRE_CH * TT : 1];
+  // Prefetch state: have_pre = the next masked row's slices are in flight to LDS;
+  // stores_after = this thread has issued a full row of gradient stores since.
+  // Vector memory operations complete in issue order, so the wait before reading
+  // the slices may leave those later stores in flight.
+  bool have_pre = false, stores_after = false;
+  auto prefetch_next = [&](int rn) {
+    if constexpr (PRE) {
+      if (rn < a.R && a.mask[rn] != 0) {
+        prefetch_row(reinterpret_cast<const uint16_t*>(tbase) + size_t(rn) * V,
+                     reinterpret_cast<const uint16_t*>(sbase) + size_t(rn) * V, V, c0, pre);
+        have_pre = true;
+        stores_after = false;
+      }
+    }
+  };
 
   for (int r = team; ok && r < a.R; r += pl.nteams) {
     E* grow = gbase ? gbase + size_t(r) * V : nullptr;
     if (a.mask[r] == 0) {
+      if (!have_pre) prefetch_next(r + pl.nteams);
       if (grow) {
         float z[EPT];
 #pragma unroll
         for (int j = 0; j < EPT; ++j) z[j] = 0.0f;
         store_grad<E, VEC>(grow, V, c0, z, z, 0.0f, 0.0f, true);
+        if (have_pre) stores_after = true;
       }
       if (member == 0 && tid == 0 && a.tv_rows) a.tv_rows[r] = 0.0f;
       continue;
     }
     float et[EPT], es[EPT];
-    load_slices<E, VEC>(tbase + size_t(r) * V, sbase + size_t(r) * V, V, c0, et, es);
+    if constexpr (PRE) {
+      if (!have_pre) {
+        prefetch_row(reinterpret_cast<const uint16_t*>(tbase) + size_t(r) * V,
+                     reinterpret_cast<const uint16_t*>(sbase) + size_t(r) * V, V, c0, pre);
+        stores_after = false;
+      }
+      if (stores_after) tv_wait_vmcnt<PRE_CH>();   // one row of gradient stores: PRE_CH per thread
+      else tv_wait_vmcnt<0>();
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < PRE_CH; ++u) {
+        float v[8];
+        TvElem<uint16_t>::unpack(pre[u * TT + tid], v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) et[u * 8 + j] = v[j];
+        TvElem<uint16_t>::unpack(pre[(PRE_CH + u) * TT + tid], v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) es[u * 8 + j] = v[j];
+      }
+      __syncthreads();
+      have_pre = false;
+      prefetch_next(r + pl.nteams);
+    } else {
+      load_slices<E, VEC>(tbase + size_t(r) * V, sbase + size_t(r) * V, V, c0, et, es);
+    }
     if (c0 + CHUNK > V) {                       // last slice of the row: mask the tail
       constexpr int VN = TvElem<E>::VN;
       const int lim = V - c0 - tid * VN;        // element j is in the row iff (j/VN)*TT*VN + j%VN < lim
@@ -335,19 +407,19 @@ __global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
           if (sh.wred[w][1] > 0.0f) Zt += double(sh.wred[w][1] * __builtin_amdgcn_exp2f((sh.wred[w][0] - Mt) * c));
           if (sh.wred[w][3] > 0.0f) Zs += double(sh.wred[w][3] * __builtin_amdgcn_exp2f((sh.wred[w][2] - Ms) * c));
         }
-        put_record(my_rec, double(Mt), Zt, double(Ms), Zs);
+        const float v[4] = {Mt, float(Zt), Ms, float(Zs)};
+        publish(my_rec, v, 4, epoch_tag | ((nbar + 1) & 0xffffu));
       }
     }
     ++nbar;
-    if (!team_barrier(ctr, nbar * unsigned(G), &hdr->abort, sh)) { ok = false; break; }
-    get_records(team_rec, G, 0, sh);
+    if (!gather(team_rec, G, 0, 4, epoch_tag | (nbar & 0xffffu), &hdr->abort, sh)) { ok = false; break; }
     if (tid == 0) {
       float Mt = -INFINITY, Ms = -INFINITY;
       double Zt = 0.0, Zs = 0.0;
-      for (int j = 0; j < G; ++j) { Mt = fmaxf(Mt, float(sh.rec[j][0])); Ms = fmaxf(Ms, float(sh.rec[j][2])); }
+      for (int j = 0; j < G; ++j) { Mt = fmaxf(Mt, sh.rec[j][0]); Ms = fmaxf(Ms, sh.rec[j][2]); }
       for (int j = 0; j < G; ++j) {
-        if (sh.rec[j][1] > 0.0) Zt += sh.rec[j][1] * double(__builtin_amdgcn_exp2f((float(sh.rec[j][0]) - Mt) * c));
-        if (sh.rec[j][3] > 0.0) Zs += sh.rec[j][3] * double(__builtin_amdgcn_exp2f((float(sh.rec[j][2]) - Ms) * c));
+        if (sh.rec[j][1] > 0.0f) Zt += double(sh.rec[j][1]) * double(__builtin_amdgcn_exp2f((sh.rec[j][0] - Mt) * c));
+        if (sh.rec[j][3] > 0.0f) Zs += double(sh.rec[j][3]) * double(__builtin_amdgcn_exp2f((sh.rec[j][2] - Ms) * c));
       }
       sh.norm[0] = Mt;
       sh.norm[1] = float(log2(Zt));
@@ -382,15 +454,14 @@ __global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       if (tid == 0) {
         double T = 0.0, Gs = 0.0;
         for (int w = 0; w < TWAVES; ++w) { T += double(sh.wred[w][0]); Gs += double(sh.wred[w][1]); }
-        __hip_atomic_store(&my_rec[4], T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&my_rec[5], Gs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float v[2] = {float(T), float(Gs)};
+        publish(my_rec + 4, v, 2, epoch_tag | ((nbar + 1) & 0xffffu));
       }
     }
     ++nbar;
-    if (!team_barrier(ctr, nbar * unsigned(G), &hdr->abort, sh)) { ok = false; break; }
-    get_records(team_rec, G, 1, sh);
+    if (!gather(team_rec, G, 1, 2, epoch_tag | (nbar & 0xffffu), &hdr->abort, sh)) { ok = false; break; }
     double tv = 0.0, gsum = 0.0;
-    for (int j = 0; j < G; ++j) { tv += sh.rec[j][0]; gsum += sh.rec[j][1]; }
+    for (int j = 0; j < G; ++j) { tv += double(sh.rec[j][0]); gsum += double(sh.rec[j][1]); }
     tv *= 0.5;
     gsum *= 0.5;
     if (member == 0 && tid == 0) {
@@ -401,10 +472,12 @@ __global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     if (grow) {
       const float h = 0.5f * inv_tn, g0 = float(-gsum * double(inv_tn));
       store_grad<E, VEC>(grow, V, c0, et, es, h, g0, false);
+      if (have_pre) stores_after = true;
     }
     __syncthreads();                           // sh.rec reuse by the next row
   }
 
+  tv_wait_vmcnt<0>();                          // no LDS prefetch left in flight
   // ---- completion: the last workgroup reduces the loss in a fixed order ----
   if (tid == 0) {
     __builtin_amdgcn_s_waitcnt(0);
@@ -427,10 +500,16 @@ __global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     *a.loss = aborted ? __builtin_nanf("") : (nresp ? float(tot / double(nresp)) : 0.0f);
     __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&hdr->abort, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.last = int(hdr->epoch + 1u);
   }
-  for (int t = tid; t < pl.nteams; t += TT)
-    __hip_atomic_store(reinterpret_cast<unsigned*>(ws + kCtrOff + size_t(t) * 64), 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  // Tags carry the epoch mod 2^16: when it wraps, clear every record so that no
+  // word left from 2^16 calls ago can match a tag of the coming calls.
+  if ((unsigned(sh.last) & 0xffffu) == 0u) {
+    unsigned long long* recs = reinterpret_cast<unsigned long long*>(ws + kRecOff);
+    for (int i = tid; i < kMaxWg * 8; i += TT) recs[i] = 0ull;
+  }
+  if (tid == 0) __hip_atomic_store(&hdr->epoch, unsigned(sh.last), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Counts the response rows and sets the loss to 0 (the main kernel overwrites it
