@@ -216,7 +216,7 @@ int uno_gated_lora_linear(const void* X, const void* W, const void* A, const voi
       return fail(UNO_ERR_UNSUPPORTED, "%s: operand %d is not 16-byte aligned", fn, i);
   const long long lim = 0x7fffffffLL;
   if ((long long)M * K * 2 > lim || (long long)N * K * 2 > lim || (long long)M * N > lim ||
-      (long long)N * r * 2 > lim)
+      (long long)N * r * 2 > lim || (long long)M * r * 2 > lim)
     return fail(UNO_ERR_UNSUPPORTED, "%s: an operand exceeds 2 GiB", fn);
   const size_t need = uno_gated_lora_linear_workspace(M, N, K, r);
   if (r > 0 && (!workspace || ws_bytes < need))

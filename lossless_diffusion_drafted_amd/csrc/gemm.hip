@@ -6,9 +6,8 @@
 //   Y = X W^T + s * diag(mask) (X A^T) B^T,   X [M,K], W [N,K], A [r,K], B [N,r].
 //
 // Two phases:
-//  1. LoRA-down T = bf16(s * X A^T): a skinny GEMM (N = r), split over K across
-//     workgroups; the last slice of each tile sums the fp32 partials in slice
-//     order (deterministic), scales and rounds.
+//  1. LoRA-down T = bf16(s * X A^T): a skinny GEMM (N = r), one workgroup per
+//     32 x 32 tile of T over the whole reduction (fixed sum order).
 //  2. The main GEMM over the extended reduction [X | T] [W | B]^T: the delta is
 //     r more reduction steps after the K steps, in the same accumulators. The row
 //     mask is applied when T's tiles are staged into LDS: rows with mask 0 are
@@ -249,125 +248,90 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams p) {
 }
 
 // LoRA-down T = bf16(scale * X A^T), X [M, K], A [r, K], T [M, r].
-// Workgroup (x, y, z): rows 32y .. 32y+31, columns 128x .. 128x+127 (wave w takes
-// 32 of them) over reduction slice z. Lanes load their MFMA fragments straight
-// from global memory (16 bytes per operand per step), LD_U steps per batch with
-// the next batch in flight. Each slice writes its fp32 partial with
-// device-coherent stores; the last slice of a tile (per-tile ticket) reads all
-// partials with device-coherent 16-byte loads, sums them in slice order, scales,
-// rounds to bf16 and resets the ticket. The result does not depend on the order
-// in which slices finish.
-constexpr int LD_ROWS = 32, LD_COLS = 128, LD_U = 8, LD_MAX_SPLITS = 16;
-constexpr int kCoherent = 16;            // buffer cache policy: device scope (sc1)
+// One workgroup per 32 x 32 tile of T, over the whole reduction, so no
+// workgroup waits for another and the sum order is fixed. Wave w of the 8 takes
+// a contiguous 1/8 of K in chunks of 64: its lanes load a chunk of the 32 X rows
+// and the 32 A rows with row-contiguous 16-byte loads (8 lanes per 128-byte row
+// segment), write it to the wave's own LDS tiles and read it back as MFMA
+// fragments, while the next three chunks' loads are in flight (the loop is
+// latency-bound otherwise). LDS operations of one
+// wave execute in order, so the wave needs no barrier. The wave partials are
+// summed in LDS in wave order, scaled and rounded.
+constexpr int LD_WAVES = 8, LD_KC = 64, LD_PITCH = LD_KC + 8;   // pitch: bf16 per LDS row
 
-__device__ __forceinline__ void ld_batch(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t ra, uint32_t xb,
-                                         uint32_t ab, bool xrow, bool arow, int k, int ke, int fh,
-                                         bf16x8_t (&xf)[LD_U], bf16x8_t (&af)[LD_U]) {
-#pragma unroll
-  for (int u = 0; u < LD_U; ++u) {
-    const int kk = k + 16 * u;
-    const bool in = kk + fh < ke;
-    xf[u] = __builtin_bit_cast(bf16x8_t,
-                               __builtin_amdgcn_raw_buffer_load_b128(rx, (xrow && in) ? xb + kk * 2 : kOutOfRange, 0u, 0));
-    af[u] = __builtin_bit_cast(bf16x8_t,
-                               __builtin_amdgcn_raw_buffer_load_b128(ra, (arow && in) ? ab + kk * 2 : kOutOfRange, 0u, 0));
-  }
-}
-
-__global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t* X, const uint16_t* A, int M, int K, int r,
-                                                        int kslice, float scale, float* part, unsigned* tickets,
-                                                        uint16_t* T) {
-  __shared__ int last;
+__global__ __launch_bounds__(LD_WAVES * 64) void lora_down_kernel(const uint16_t* X, const uint16_t* A, int M,
+                                                                  int K, int r, float scale, uint16_t* T) {
+  constexpr int TILE = 32 * LD_PITCH;                 // bf16 per operand tile
+  constexpr int STAGE_BYTES = LD_WAVES * 2 * TILE * 2;
+  constexpr int RED_BYTES = LD_WAVES * 16 * 64 * 4;
+  __shared__ __attribute__((aligned(16))) char smem[STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES];
+  // Tiles of the same 32 X rows go to consecutive ids on one XCD (workgroups
+  // are dealt to the 8 XCDs round robin), so each XCD's L2 fetches those rows once.
+  const int ttc = (r + 31) / 32;
+  const int tid_x = xcd_contiguous_id(int(blockIdx.x), int(gridDim.x));
+  const int tm = tid_x / ttc, tc = tid_x % ttc;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m0 = blockIdx.y * LD_ROWS, cb = blockIdx.x * LD_COLS, c0 = cb + wave * 32;
-  const int splits = gridDim.z, z = blockIdx.z;
-  const int kb = z * kslice, ke = min(K, kb + kslice);
-  const int fr = lane & 31, fh = (lane >> 5) * 8;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem) + wave * 2 * TILE;
+  uint16_t* as = xs + TILE;
   const __amdgpu_buffer_rsrc_t rx = make_row_rsrc(X, uint32_t(size_t(M) * K * 2));
   const __amdgpu_buffer_rsrc_t ra = make_row_rsrc(A, uint32_t(size_t(r) * K * 2));
-  const bool xrow = m0 + fr < M, arow = c0 + fr < r;
-  const uint32_t xb = uint32_t((size_t(m0 + fr) * K + fh) * 2);
-  const uint32_t ab = uint32_t((size_t(c0 + fr) * K + fh) * 2);
+  // Loads: lane l covers rows l / 8 + 8 j (j < 4) at k offset 8 (l % 8).
+  const int lr = lane >> 3, lk = (lane & 7) * 8;
+  const int kw = (K + LD_WAVES * LD_KC - 1) / (LD_WAVES * LD_KC) * LD_KC;
+  const int kb = wave * kw, ke = min(K, kb + kw);
+  constexpr int NB = 4;                               // chunks in flight
+  u32x4_t xv[NB][4], av[NB][4];
+  auto load = [&](int k, u32x4_t (&xb)[4], u32x4_t (&ab)[4]) {
+    const bool in = k + lk < ke;                     // ke is a multiple of 8
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int xrow = tm * 32 + lr + 8 * j, arow = tc * 32 + lr + 8 * j;
+      xb[j] = __builtin_amdgcn_raw_buffer_load_b128(
+          rx, (in && xrow < M) ? uint32_t((size_t(xrow) * K + k + lk) * 2) : kOutOfRange, 0u, 0);
+      ab[j] = __builtin_amdgcn_raw_buffer_load_b128(
+          ra, (in && arow < r) ? uint32_t((size_t(arow) * K + k + lk) * 2) : kOutOfRange, 0u, 0);
+    }
+  };
   f32x16_t acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  bf16x8_t x0[LD_U], a0[LD_U], x1[LD_U], a1[LD_U];
-  ld_batch(rx, ra, xb, ab, xrow, arow, kb, ke, fh, x0, a0);
-  for (int k = kb; k < ke; k += 32 * LD_U) {
-    ld_batch(rx, ra, xb, ab, xrow, arow, k + 16 * LD_U, ke, fh, x1, a1);
+  // Fragments: lane l reads row l % 32, k = 16 ks + 8 (l / 32) .. +7.
+  const int fo = (lane & 31) * LD_PITCH + (lane >> 5) * 8;
 #pragma unroll
-    for (int u = 0; u < LD_U; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x0[u], a0[u], acc, 0, 0, 0);
-    ld_batch(rx, ra, xb, ab, xrow, arow, k + 32 * LD_U, ke, fh, x0, a0);
+  for (int b = 0; b < NB - 1; ++b) load(kb + b * LD_KC, xv[b], av[b]);
+  // Chunks past the range load zeros (out of range) and add nothing.
+  for (int k0 = kb; k0 < ke; k0 += NB * LD_KC) {
 #pragma unroll
-    for (int u = 0; u < LD_U; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x1[u], a1[u], acc, 0, 0, 0);
-  }
-  // Partial of this slice, as [split][M][rpad] (rpad = r rounded up to 128, so the
-  // reduction reads whole 16-byte groups). Accumulator v sits at row
-  // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
-  const int rpad = gridDim.x * LD_COLS;
-  const size_t plane = size_t(M) * rpad;
-  const __amdgpu_buffer_rsrc_t rp = make_row_rsrc(part, uint32_t(size_t(splits) * plane * 4));
+    for (int b = 0; b < NB; ++b) {
+      const int k = k0 + b * LD_KC;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int row = m0 + 8 * (v >> 2) + (fh >> 1) + (v & 3);
-    const uint32_t off = row < M ? uint32_t((z * plane + size_t(row) * rpad + c0 + fr) * 4) : kOutOfRange;
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[v]), rp, off, 0u, kCoherent);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  unsigned* ticket = tickets + blockIdx.y * gridDim.x + blockIdx.x;
-  if (threadIdx.x == 0)
-    last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == unsigned(splits - 1);
-  __syncthreads();
-  if (!last) return;
-  // 32 x 128 tile = 1024 groups of 4 columns; 4 groups per thread, every split's
-  // loads issued before any is summed.
+      for (int j = 0; j < 4; ++j) {
+        *reinterpret_cast<u32x4_t*>(xs + (lr + 8 * j) * LD_PITCH + lk) = xv[b][j];
+        *reinterpret_cast<u32x4_t*>(as + (lr + 8 * j) * LD_PITCH + lk) = av[b][j];
+      }
+      load(k + (NB - 1) * LD_KC, xv[(b + NB - 1) % NB], av[(b + NB - 1) % NB]);
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int gi = threadIdx.x + g * 256;
-    const int row = m0 + gi / (LD_COLS / 4), col = cb + (gi % (LD_COLS / 4)) * 4;
-    u32x4_t v[LD_MAX_SPLITS];
-#pragma unroll
-    for (int zz = 0; zz < LD_MAX_SPLITS; ++zz) {
-      const uint32_t off = (zz < splits && row < M) ? uint32_t((zz * plane + size_t(row) * rpad + col) * 4) : kOutOfRange;
-      v[zz] = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0u, kCoherent);
-    }
-    float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int zz = 0; zz < LD_MAX_SPLITS; ++zz) {
-      if (zz < splits) {
-        sum[0] += __uint_as_float(v[zz].x);
-        sum[1] += __uint_as_float(v[zz].y);
-        sum[2] += __uint_as_float(v[zz].z);
-        sum[3] += __uint_as_float(v[zz].w);
+      for (int ks = 0; ks < LD_KC / 16; ++ks) {
+        const bf16x8_t xf = *reinterpret_cast<const bf16x8_t*>(xs + fo + ks * 16);
+        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(as + fo + ks * 16);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, af, acc, 0, 0, 0);
       }
     }
-    if (row < M) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (col + e < r) T[size_t(row) * r + col + e] = __builtin_bit_cast(uint16_t, (__bf16)(scale * sum[e]));
-    }
   }
-  if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-struct Plan {
-  int tx, ty, splits, kslice;
-};
-
-// LoRA-down grid: about 256 workgroups, reduction slices of at least 128.
-Plan lora_plan(int M, int K, int r) {
-  Plan pl;
-  pl.tx = (r + LD_COLS - 1) / LD_COLS;
-  pl.ty = (M + LD_ROWS - 1) / LD_ROWS;
-  int splits = 256 / (pl.tx * pl.ty);
-  const int max_splits = (K + 127) / 128;
-  if (splits > max_splits) splits = max_splits;
-  if (splits > LD_MAX_SPLITS) splits = LD_MAX_SPLITS;
-  if (splits < 1) splits = 1;
-  pl.kslice = ((K + splits - 1) / splits + 15) / 16 * 16;
-  pl.splits = (K + pl.kslice - 1) / pl.kslice;
-  return pl;
+  __syncthreads();                                    // the stage tiles become the reduction buffer
+  float* red = reinterpret_cast<float*>(smem);        // [wave][v][lane]
+#pragma unroll
+  for (int v = 0; v < 16; ++v) red[(wave * 16 + v) * 64 + lane] = acc[v];
+  __syncthreads();
+  // Accumulator v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
+  for (int i = threadIdx.x; i < 16 * 64; i += LD_WAVES * 64) {
+    const int v = i >> 6, l = i & 63;
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < LD_WAVES; ++w) sum += red[(w * 16 + v) * 64 + l];
+    const int row = tm * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3), col = tc * 32 + (l & 31);
+    if (row < M && col < r) T[size_t(row) * r + col] = __builtin_bit_cast(uint16_t, (__bf16)(scale * sum));
+  }
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -390,26 +354,21 @@ bool use_wide(int M, int N) {
 
 size_t gemm_workspace_bytes(int M, int N, int K, int r) {
   (void)N;
+  (void)K;
   if (r <= 0 || M <= 0) return 256;
-  const Plan pl = lora_plan(M, K, r);
-  return align256(size_t(pl.tx) * pl.ty * 4) + align256(size_t(pl.splits) * M * pl.tx * LD_COLS * 4) +
-         align256(size_t(M) * r * 2);
+  return align256(size_t(M) * r * 2);             // T
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   const uint16_t* tmat = nullptr;
   if (a.r > 0) {
-    // workspace: [tickets (left at zero by every call) | fp32 partials | T bf16 [M, r]]
-    const Plan pl = lora_plan(a.M, a.K, a.r);
-    char* ws = static_cast<char*>(a.ws);
-    unsigned* tickets = reinterpret_cast<unsigned*>(ws);
-    const size_t off_part = align256(size_t(pl.tx) * pl.ty * 4);
-    float* part = reinterpret_cast<float*>(ws + off_part);
-    uint16_t* t = reinterpret_cast<uint16_t*>(ws + off_part + align256(size_t(pl.splits) * a.M * pl.tx * LD_COLS * 4));
-    hipLaunchKernelGGL(lora_down_kernel, dim3(pl.tx, pl.ty, pl.splits), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(a.X), static_cast<const uint16_t*>(a.A), a.M, a.K, a.r,
-                       pl.kslice, a.scale, part, tickets, t);
+    // workspace: T bf16 [M, r]
+    uint16_t* t = static_cast<uint16_t*>(a.ws);
+    const unsigned tiles = unsigned((a.M + 31) / 32) * unsigned((a.r + 31) / 32);
+    hipLaunchKernelGGL(lora_down_kernel, dim3(tiles), dim3(LD_WAVES * 64), 0, stream,
+                       static_cast<const uint16_t*>(a.X), static_cast<const uint16_t*>(a.A), a.M, a.K, a.r, a.scale,
+                       t);
     tmat = t;
   }
   GemmParams g{};

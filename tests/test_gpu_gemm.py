@@ -127,3 +127,19 @@ def test_argument_errors():
     with pytest.raises(uno.UnoError) as e:
         uno.uno_gated_lora_linear(X, W, A, B, m, 1.0)      # K = 12 is not a multiple of 8
     assert e.value.status == "UNO_ERR_UNSUPPORTED"
+
+
+def test_alternating_shapes_share_the_workspace():
+    """Calls of different shapes reuse one workspace, whose split-K counters carry
+    over from call to call: results must not depend on what ran before."""
+    shapes = [(512, 2560, 640, 64), (1024, 4096, 384, 128), (200, 1000, 72, 24)]
+    runs = []
+    for M, K, N, r in shapes:
+        X, W, A, B = workloads.gemm_inputs(M, K, N, r, seed=5)
+        args = [to_device(a, DEV) for a in (X, W, A, B)]
+        mask = to_device(workloads.noise_row_mask(M // 8, 8) if M % 8 == 0 else np.ones(M, np.uint8), DEV)
+        runs.append((args, mask))
+    first = [_bits(_run(*args, mask, 16.0)) for args, mask in runs]
+    for _ in range(2):
+        for (args, mask), ref in zip(reversed(runs), reversed(first)):
+            np.testing.assert_array_equal(_bits(_run(*args, mask, 16.0)), ref)
