@@ -1341,7 +1341,12 @@ __global__ __launch_bounds__(VT) void verify_kernel(VerifyArgs a) {
   last = readlane_i(last, 0);
   if (last) {
     unsigned long long r = 0x100000000ull | 0xffffffffull;   // (tok -1, acc 1)
-    if (tid < b) r = __hip_atomic_load(&rec[size_t(s) * b + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < b) {
+      // Records are cleared once read, so the whole workspace is zero again at
+      // the end of the call (a later call may lay it out differently).
+      r = __hip_atomic_load(&rec[size_t(s) * b + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&rec[size_t(s) * b + tid], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     const int rtok = int(unsigned(r & 0xffffffffull));
     const int racc = int(r >> 32);
     const unsigned long long rej = __ballot(tid >= 1 && tid < b && racc == 0);

@@ -246,3 +246,15 @@ def test_greedy_ties_take_the_lowest_id():
     st, gpu, ref = _run_full(z, z.copy(), dict(SP, temperature=0.0))
     assert st["exact"] == S
     assert gpu["out_tokens"][0, 0] == 500
+
+
+def test_workspace_reuse_across_shapes():
+    """Calls of different shapes share one workspace. A call with more sequences
+    lays its per-sequence counters over what an earlier call used for slot
+    records, so every call must leave the workspace clear."""
+    sp = dict(SP)
+    for S, b in [(8, 16), (96, 1), (8, 16), (40, 3)]:
+        cfg = dict(workloads.VERIFY_CONFIGS["qwen"], S=S, b=b)
+        p, q = workloads.verify_logits(cfg, seed=S * 100 + b, V=4096)
+        st, gpu, ref = _run_full(p, q, sp)
+        assert st["exact"] + st["near_tie"] == S and st["exact"] >= S - 1, (S, b, st)
