@@ -361,7 +361,9 @@ __device__ __forceinline__ void stream_two(const RowView<E, true>& pv, const Row
     pv.load_tile(A, t + 1);
     process_tile(qv, Rq, B, t, sq);
     qv.load_tile(B, t + 1);
-    if (bounded && (t == 1 || t == 3 || t == 7)) {
+    // The bound rises fastest early on, when each tile adds many lane maxima:
+    // refreshing it after each of the first 8 tiles keeps fewer candidates.
+    if (bounded && t < 8) {
       sp.thr = refresh_bound(Rp, sp, c, sh);
       sq.thr = refresh_bound(Rq, sq, c, sh);
     }
