@@ -11,9 +11,10 @@ come from the library's draft sampler before the timed region.
 Also reported: per-kernel average durations from HIP events on the launch
 stream, the roofline fraction of the dominant kernel, the TV loss kernel on the
 self-distillation workload (8 x 4096 rows, vocabulary 151936) as a separate leg,
-and the CPU oracle timed on a bounded sample of the same verify workload.
+verification alone at block 16 and block 8 with sampled and greedy decoding, and
+the CPU oracle timed on a bounded sample of the same verify workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-tv]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-tv] [--no-sweep]
 
 Counter runs (rocprofv3 --pmc) time one kernel alone:
   python bench.py --only {verify,gemm_attn,gemm_mlp,tv,copy} --steps K
@@ -59,6 +60,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-tv", action="store_true", help="skip the TV-loss leg")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the verify block-size / greedy sweep")
     ap.add_argument("--only", choices=sorted(list(ONLY) + ["copy"]),
                     help="run one kernel alone (for counter runs) and print its timing")
     ap.add_argument("--summarize-pmc", metavar="DIR", help="write profiles/KERNEL_traffic.md from counter CSVs")
@@ -347,6 +349,10 @@ def main():
         roof = dict(bound="mfma", achieved=k["TFLOPs"], peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=k["mfma_frac"], traffic=traffic, kernel=dominant)
 
+    sweep = None
+    if not args.no_sweep:
+        sweep = verify_sweep(uno, workloads, p_np, q_np, dev, max(10, args.steps))
+
     tv_leg = None
     if not args.no_tv:
         tv_leg = tv_benchmark(uno, workloads, dev, max(3, args.steps // 4))
@@ -378,6 +384,8 @@ def main():
         "mean_accept_len": acc.mean().item(),
         "cpu_baseline": cpu,
     }
+    if sweep is not None:
+        line["verify_sweep"] = sweep
     if tv_leg is not None:
         line["tv_loss"] = tv_leg
     print(json.dumps(line))
@@ -408,6 +416,42 @@ def tv_benchmark(uno, workloads, dev, iters):
                avg_us=ms * 1000, bytes=byts, GBps=byts / (ms * 1e6), hbm_frac=byts / (ms * 1e6) / HBM_PEAK_GBS,
                loss=loss.item())
     del t, s, grad
+    torch.cuda.empty_cache()
+    return out
+
+
+def verify_sweep(uno, workloads, p_np, q_np, dev, iters):
+    """Verify at the metric's shape (64 sequences, V = 151936) for block 16 and block 8
+    (the first 8 slots of each block) and for sampled (T = 1, top-k 50, top-p 0.95)
+    and greedy (T = 0) decoding."""
+    import numpy as np
+    import torch
+    S, V = p_np.shape[0], p_np.shape[2]
+    seq = dev_tensor(np.arange(S, dtype=np.int64), dev)
+    pos = dev_tensor(np.zeros(S, dtype=np.int64), dev)
+    out = {}
+    for b in (16, 8):
+        p = dev_tensor(np.ascontiguousarray(p_np[:, :b]), dev)
+        q = dev_tensor(np.ascontiguousarray(q_np[:, :b]), dev)
+        for label, sp in (("sampled", workloads.SAMPLING), ("greedy", dict(workloads.SAMPLING, temperature=0.0))):
+            draft, _ = uno.uno_draft_sample(q, seq, pos, **sp)
+            outs = dict(out_tokens=torch.empty((S, b), dtype=torch.int32, device=dev),
+                        accept_len=torch.empty((S,), dtype=torch.int32, device=dev),
+                        resampled=torch.empty((S,), dtype=torch.int32, device=dev))
+            fn = lambda: uno.uno_verify_block(p, q, draft, seq, pos, want_slot_accept=False, want_diag=False,
+                                              out=outs, **sp)
+            timer = KernelTimer()
+            fn()
+            torch.cuda.synchronize()
+            for _ in range(iters):
+                timer.run("v", fn)
+            torch.cuda.synchronize()
+            ms = timer.avg_ms("v")
+            byts = verify_bytes(S, b, V)
+            out[f"b{b}_{label}"] = dict(avg_us=ms * 1000, positions_per_s=S * b / (ms / 1000),
+                                        GBps=byts / (ms * 1e6), hbm_frac=byts / (ms * 1e6) / HBM_PEAK_GBS,
+                                        mean_accept_len=outs["accept_len"].float().mean().item())
+        del p, q
     torch.cuda.empty_cache()
     return out
 

@@ -139,28 +139,38 @@ def test_empty_batch_is_a_no_op():
     assert r["accept_len"].numel() == 0
 
 
-@pytest.mark.parametrize("name,nsample", [("qwen", 6), ("looped", 6), ("stress", 4)])
-def test_verify_full_size_sampled(name, nsample):
+GREEDY = dict(SP, temperature=0.0)
+
+
+@pytest.mark.parametrize("name,nsample,sp,b", [
+    ("qwen", 6, SP, None), ("looped", 6, SP, None), ("stress", 4, SP, None),
+    ("qwen", 6, GREEDY, None),          # greedy decoding at the metric's shape
+    ("qwen", 6, SP, 8),                 # block 8 at the metric's shape
+])
+def test_verify_full_size_sampled(name, nsample, sp, b):
     """Full-size workload in the benchmark's launch configuration; the oracle checks a
     seeded sample of sequences."""
     uno = _uno()
     c = workloads.VERIFY_CONFIGS[name]
-    S, b, V = c["S"], c["b"], c["V"]
+    S, V = c["S"], c["V"]
     p, q = workloads.verify_logits(name)
+    if b is not None:                   # the first b slots of each block
+        p, q = np.ascontiguousarray(p[:, :b]), np.ascontiguousarray(q[:, :b])
+    b = p.shape[1]
     seq, pos = np.arange(S, dtype=np.int64), np.zeros(S, dtype=np.int64)
     pd, qd = to_device(p, DEV), to_device(q, DEV)
-    dg, _ = uno.uno_draft_sample(qd, to_device(seq, DEV), to_device(pos, DEV), **SP)
+    dg, _ = uno.uno_draft_sample(qd, to_device(seq, DEV), to_device(pos, DEV), **sp)
     torch.cuda.synchronize()
     d = dg.cpu().numpy()
     pick = np.sort(np.random.default_rng(0).choice(S, nsample, replace=False))
-    dref, _ = oracle.draft_sample(q[pick], seq[pick], pos[pick], SP["temperature"], SP["top_k"],
-                                  SP["top_p"], SP["seed"], "bf16")
+    dref, _ = oracle.draft_sample(q[pick], seq[pick], pos[pick], sp["temperature"], sp["top_k"],
+                                  sp["top_p"], sp["seed"], "bf16")
     tie_free = np.array_equal(dref, d[pick])
     d[pick] = dref                      # oracle drafts on the compared sequences
-    ref = oracle.verify_block(p[pick], q[pick], dref, seq[pick], pos[pick], SP["temperature"],
-                              SP["top_k"], SP["top_p"], SP["seed"], "bf16")
+    ref = oracle.verify_block(p[pick], q[pick], dref, seq[pick], pos[pick], sp["temperature"],
+                              sp["top_k"], sp["top_p"], sp["seed"], "bf16")
     r = uno.uno_verify_block(pd, qd, to_device(d.astype(np.int32), DEV), to_device(seq, DEV),
-                             to_device(pos, DEV), **SP)
+                             to_device(pos, DEV), **sp)
     torch.cuda.synchronize()
     gpu = {k: v.cpu().numpy() for k, v in r.items()}
     st = compare_verify(gpu, ref, b, seqs=pick)
