@@ -18,4 +18,4 @@ from .sampling import (  # noqa: F401
     filter_logits, inverse_cdf, verify_block,
 )
 from .tv import tv_loss_fwd_bwd  # noqa: F401
-from .gated_lora import bf16_bits_to_f64, gated_lora_linear, lora_delta  # noqa: F401
+from .gated_lora import bf16_bits_to_f64, gated_lora_linear, gated_lora_linear_bwd, lora_delta  # noqa: F401

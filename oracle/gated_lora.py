@@ -44,3 +44,30 @@ def lora_delta(X, A, B, scale):
     a = bf16_bits_to_f64(A)
     bb = bf16_bits_to_f64(B)
     return scale * ((x @ a.T) @ bb.T)
+
+
+def gated_lora_linear_bwd(X, W, A, B, row_mask, scale, dY):
+    """fp64 gradients (dX [M,K], dA [r,K], dB [N,r]) of the row-gated LoRA linear for
+    an upstream gradient dY [M,N]; the frozen base weight W gets none.
+
+    The adapter is trained by self-distillation on the noise rows only ("LoopUno",
+    "How it works" -> "Training is self-distillation"; "Setup / Recipe": gated LoRA
+    on the noise rows). By the chain rule on Y = X W^T + s diag(m) (X A^T) B^T:
+
+        U  = s diag(m) dY B            [M, r]
+        dX = dY W + U A                [M, K]
+        dA = U^T X                     [r, K]
+        dB = s (diag(m) dY)^T (X A^T)  [N, r]
+    """
+    x = bf16_bits_to_f64(X)
+    w = bf16_bits_to_f64(W)
+    a = bf16_bits_to_f64(A)
+    bb = bf16_bits_to_f64(B)
+    g = bf16_bits_to_f64(dY)
+    m = np.asarray(row_mask).astype(np.float64)
+    gm = m[:, None] * g
+    u = scale * (gm @ bb)
+    dx = g @ w + u @ a
+    da = u.T @ x
+    db = scale * (gm.T @ (x @ a.T))
+    return dx, da, db

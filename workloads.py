@@ -137,6 +137,11 @@ def gemm_inputs(M, K, N, r, seed=0, tag=0):
     return X, W, A, B
 
 
+def gemm_grad(M, N, seed=0, tag=0):
+    """bf16 bit patterns of an upstream gradient dY [M,N] ~ N(0, 0.01^2)."""
+    return to_bf16_bits(np.float32(0.01) * _rng(seed, 101, tag, 0, M, N).standard_normal((M, N), dtype=np.float32))
+
+
 def tv_response_mask(n_seq, seq_len, resp_len):
     m = np.zeros((n_seq, seq_len), dtype=np.uint8)
     m[:, seq_len - resp_len:] = 1
