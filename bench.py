@@ -11,8 +11,9 @@ come from the library's draft sampler before the timed region.
 Also reported: per-kernel average durations from HIP events on the launch
 stream, the roofline fraction of the dominant kernel, the TV loss kernel on the
 self-distillation workload (8 x 4096 rows, vocabulary 151936) as a separate leg,
-verification alone at block 16 and block 8 with sampled and greedy decoding, and
-the CPU oracle timed on a bounded sample of the same verify workload.
+verification alone at block 16 and block 8 with sampled and greedy decoding, the
+gated-LoRA backward on both projections, and the CPU oracle timed on a bounded
+sample of the same verify workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-tv] [--no-sweep]
 
@@ -60,7 +61,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-tv", action="store_true", help="skip the TV-loss leg")
-    ap.add_argument("--no-sweep", action="store_true", help="skip the verify block-size / greedy sweep")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the verify block-size / greedy sweep and the gated-LoRA backward leg")
     ap.add_argument("--only", choices=sorted(list(ONLY) + ["copy"]),
                     help="run one kernel alone (for counter runs) and print its timing")
     ap.add_argument("--summarize-pmc", metavar="DIR", help="write profiles/KERNEL_traffic.md from counter CSVs")
@@ -349,6 +351,10 @@ def main():
         roof = dict(bound="mfma", achieved=k["TFLOPs"], peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=k["mfma_frac"], traffic=traffic, kernel=dominant)
 
+    bwd = None
+    if not args.no_sweep:
+        bwd = lora_bwd_benchmark(uno, workloads, dev, max(10, args.steps))
+
     sweep = None
     if not args.no_sweep:
         sweep = verify_sweep(uno, workloads, p_np, q_np, dev, max(10, args.steps))
@@ -386,6 +392,8 @@ def main():
     }
     if sweep is not None:
         line["verify_sweep"] = sweep
+    if bwd is not None:
+        line["gated_lora_bwd"] = bwd
     if tv_leg is not None:
         line["tv_loss"] = tv_leg
     print(json.dumps(line))
@@ -416,6 +424,34 @@ def tv_benchmark(uno, workloads, dev, iters):
                avg_us=ms * 1000, bytes=byts, GBps=byts / (ms * 1e6), hbm_frac=byts / (ms * 1e6) / HBM_PEAK_GBS,
                loss=loss.item())
     del t, s, grad
+    torch.cuda.empty_cache()
+    return out
+
+
+def lora_bwd_benchmark(uno, workloads, dev, iters):
+    """The gated-LoRA backward (dX, dA, dB) on both Qwen-shaped projections."""
+    import torch
+    gcfg = workloads.GEMM_CONFIGS["qwen"]
+    M, r = gcfg["M"], gcfg["r"]
+    mask = dev_tensor(workloads.noise_row_mask(M // gcfg["b"], gcfg["b"]), dev)
+    out = {}
+    for gi, (name, K, N) in enumerate(gcfg["projections"]):
+        X, W, A, B = (dev_tensor(a, dev) for a in workloads.gemm_inputs(M, K, N, r, tag=gi))
+        G = dev_tensor(workloads.gemm_grad(M, N, tag=gi), dev)
+        fn = lambda: uno.uno_gated_lora_linear_bwd(G, X, W, A, B, mask, 1.0)
+        fn()
+        torch.cuda.synchronize()
+        timer = KernelTimer()
+        for _ in range(iters):
+            timer.run("b", fn)
+        torch.cuda.synchronize()
+        ms = timer.avg_ms("b")
+        # dX = dY W + U A, U = dY B, T = X A^T, dA = U^T X, dB = dY^T T
+        flops = 2.0 * M * N * K + 2.0 * M * r * K + 2.0 * M * N * r + 2.0 * M * K * r + 2.0 * r * M * K + \
+            2.0 * N * M * r
+        out[f"gated_lora_bwd_{name}"] = dict(avg_us=ms * 1000, flops=flops, TFLOPs=flops / (ms * 1e9),
+                                                    mfma_frac=flops / (ms * 1e9) / BF16_PEAK_TFLOPS)
+        del X, W, A, B, G
     torch.cuda.empty_cache()
     return out
 

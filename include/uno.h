@@ -183,6 +183,31 @@ int uno_gated_lora_linear(const void* X, const void* W, const void* A, const voi
                           int M, int N, int K, int r,
                           void* workspace, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Backward of the row-gated LoRA linear ("LoopUno", "How it works" -> "Training
+ * is self-distillation" and "Setup / Recipe": the adapter, switched on for the
+ * noise rows only, is what training updates; the base weight W stays frozen).
+ * For an upstream gradient dY of Y = X W^T + s diag(m) (X A^T) B^T:
+ *   U  = bf16(s diag(m) dY B)            [M, r]
+ *   dX = dY W + U A                      [M, K]
+ *   dA = U^T X                           [r, K]
+ *   dB = s (diag(m) dY)^T (X A^T)        [N, r]
+ * bf16 in, fp32 accumulation, bf16 out; X A^T is rounded to bf16 before it meets
+ * dY, as U is before it meets A and X.
+ *   dY : bf16 [M, N]; X, W, A, B, row_mask, scale : as for the forward
+ *   dX : bf16 [M, K] (out, optional: NULL skips it); dA : bf16 [r, K] (out);
+ *   dB : bf16 [N, r] (out); outputs must not alias inputs or each other
+ *   workspace : >= uno_gated_lora_linear_bwd_workspace(M, N, K, r) bytes (it
+ *   holds transposed copies of W, X, dY and the rank-r factors)
+ * Limits: M, N, K, r >= 1; M, N, K and r multiples of 8 and all row starts
+ * 16-byte aligned (UNO_ERR_UNSUPPORTED otherwise).
+ * ------------------------------------------------------------------------- */
+size_t uno_gated_lora_linear_bwd_workspace(int M, int N, int K, int r);
+int uno_gated_lora_linear_bwd(const void* dY, const void* X, const void* W, const void* A,
+                              const void* B, const uint8_t* row_mask, float scale,
+                              void* dX, void* dA, void* dB, int M, int N, int K, int r,
+                              void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -8,7 +8,7 @@ from ._lib import (FLAG_OVERFLOW, FLAG_Q_ZERO, FLAG_RES_ZERO, FLAG_TIE_ACCEPT,  
                    FLAG_TIE_ICDF, FLAG_TIE_MASK, FLAG_TIE_TOPP_P, FLAG_TIE_TOPP_Q,
                    LIB_PATH, UnoError, load)
 from .ops import (sampling_params, uno_draft_sample, uno_gated_lora_linear,  # noqa: F401
-                  uno_tv_loss_fwd_bwd, uno_verify_block)
+                  uno_gated_lora_linear_bwd, uno_tv_loss_fwd_bwd, uno_verify_block)
 
 __all__ = ["uno_verify_block", "uno_draft_sample", "uno_tv_loss_fwd_bwd",
-           "uno_gated_lora_linear", "sampling_params", "load", "UnoError", "LIB_PATH"]
+           "uno_gated_lora_linear", "uno_gated_lora_linear_bwd", "sampling_params", "load", "UnoError", "LIB_PATH"]

@@ -34,6 +34,7 @@ EXPORTS = [
     "uno_verify_block_workspace", "uno_verify_block", "uno_draft_sample",
     "uno_tv_loss_workspace", "uno_tv_loss_fwd_bwd",
     "uno_gated_lora_linear_workspace", "uno_gated_lora_linear",
+    "uno_gated_lora_linear_bwd_workspace", "uno_gated_lora_linear_bwd",
 ]
 
 
@@ -83,6 +84,9 @@ def load():
             "uno_gated_lora_linear_workspace": (_SZ, [_I, _I, _I, _I]),
             "uno_gated_lora_linear": (_I, [_P, _P, _P, _P, _P, ctypes.c_float, _P, _I, _I, _I,
                                            _I, _P, _SZ, _P]),
+            "uno_gated_lora_linear_bwd_workspace": (_SZ, [_I, _I, _I, _I]),
+            "uno_gated_lora_linear_bwd": (_I, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _I, _I,
+                                               _I, _I, _P, _SZ, _P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)

@@ -237,4 +237,52 @@ int uno_gated_lora_linear(const void* X, const void* W, const void* A, const voi
   return hip_status(uno::launch_gemm(a, static_cast<hipStream_t>(stream)), "uno_gated_lora_linear launch");
 }
 
+size_t uno_gated_lora_linear_bwd_workspace(int M, int N, int K, int r) {
+  if (M <= 0 || N <= 0 || K <= 0 || r <= 0) return 256;
+  return uno::gemm_bwd_workspace_bytes(M, N, K, r);
+}
+
+int uno_gated_lora_linear_bwd(const void* dY, const void* X, const void* W, const void* A, const void* B,
+                              const uint8_t* row_mask, float scale, void* dX, void* dA, void* dB, int M, int N,
+                              int K, int r, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "uno_gated_lora_linear_bwd";
+  if (M < 0 || N < 1 || K < 1 || r < 1)
+    return fail(UNO_ERR_INVALID_ARG, "%s: sizes M = %d, N = %d, K = %d, r = %d out of range", fn, M, N, K, r);
+  if (!isfinite(scale)) return fail(UNO_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (M == 0) return ok();
+  if (!dY || !X || !W || !A || !B || !row_mask || !dA || !dB)
+    return fail(UNO_ERR_INVALID_ARG, "%s: only dX may be null", fn);
+  if (M % 8 != 0 || N % 8 != 0 || K % 8 != 0 || r % 8 != 0)
+    return fail(UNO_ERR_UNSUPPORTED, "%s: M = %d, N = %d, K = %d and r = %d must be multiples of 8", fn, M, N,
+                K, r);
+  const void* ptrs[8] = {dY, X, W, A, B, dX, dA, dB};
+  for (int i = 0; i < 8; ++i)
+    if (ptrs[i] && reinterpret_cast<uintptr_t>(ptrs[i]) % 16 != 0)
+      return fail(UNO_ERR_UNSUPPORTED, "%s: operand %d is not 16-byte aligned", fn, i);
+  const long long lim = 0x7fffffffLL;
+  if ((long long)M * K * 2 > lim || (long long)N * K * 2 > lim || (long long)M * N * 2 > lim ||
+      (long long)N * r * 2 > lim || (long long)M * r * 2 > lim || (long long)K * r * 2 > lim)
+    return fail(UNO_ERR_UNSUPPORTED, "%s: an operand exceeds 2 GiB", fn);
+  const size_t need = uno_gated_lora_linear_bwd_workspace(M, N, K, r);
+  if (!workspace || ws_bytes < need)
+    return fail(UNO_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, need);
+  uno::GemmBwdArgs a;
+  a.dY = dY;
+  a.X = X;
+  a.W = W;
+  a.A = A;
+  a.B = B;
+  a.row_mask = row_mask;
+  a.scale = scale;
+  a.dX = dX;
+  a.dA = dA;
+  a.dB = dB;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.r = r;
+  a.ws = workspace;
+  return hip_status(uno::launch_gemm_bwd(a, static_cast<hipStream_t>(stream)), "uno_gated_lora_linear_bwd launch");
+}
+
 }  // extern "C"

@@ -332,7 +332,8 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams p) {
 constexpr int LD_WAVES = 8, LD_KC = 64, LD_PITCH = LD_KC + 8;   // pitch: bf16 per LDS row
 
 __global__ __launch_bounds__(LD_WAVES * 64) void lora_down_kernel(const uint16_t* X, const uint16_t* A, int M,
-                                                                  int K, int r, float scale, uint16_t* T) {
+                                                                  int K, int r, float scale, uint16_t* T,
+                                                                  const uint8_t* row_mask) {
   constexpr int TILE = 32 * LD_PITCH;                 // bf16 per operand tile
   constexpr int STAGE_BYTES = LD_WAVES * 2 * TILE * 2;
   constexpr int RED_BYTES = LD_WAVES * 16 * 64 * 4;
@@ -402,8 +403,83 @@ __global__ __launch_bounds__(LD_WAVES * 64) void lora_down_kernel(const uint16_t
 #pragma unroll
     for (int w = 0; w < LD_WAVES; ++w) sum += red[(w * 16 + v) * 64 + l];
     const int row = tm * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3), col = tc * 32 + (l & 31);
-    if (row < M && col < r) T[size_t(row) * r + col] = __builtin_bit_cast(uint16_t, (__bf16)(scale * sum));
+    if (row < M && col < r) {
+      const float y = (row_mask && row_mask[row] == 0) ? 0.0f : scale * sum;   // masked rows: exact zeros
+      T[size_t(row) * r + col] = __builtin_bit_cast(uint16_t, (__bf16)y);
+    }
   }
+}
+
+// Transpose of a bf16 matrix: dst [C, R] = src [R, C]^T, with source rows whose
+// mask byte is 0 written as zeros and, when scale != 1, every value scaled and
+// rounded to nearest even. 64 x 64 tiles through LDS; 16-byte loads and stores
+// when R and C are multiples of 8 (and the buffers 16-byte aligned), element
+// accesses otherwise.
+constexpr int TP = 64, TP_PITCH = TP + 8;
+
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* src, int R, int C, uint16_t* dst,
+                                                         const uint8_t* row_mask, float scale, int vec) {
+  __shared__ uint16_t t[TP][TP_PITCH];
+  const int r0 = blockIdx.y * TP, c0 = blockIdx.x * TP;
+  const int tid = threadIdx.x, lr = tid >> 3, lc = (tid & 7) * 8;
+  auto cvt = [&](uint16_t h, bool keep) -> uint16_t {
+    if (!keep) return 0;
+    if (scale == 1.0f) return h;
+    return __builtin_bit_cast(uint16_t, (__bf16)(scale * __uint_as_float(uint32_t(h) << 16)));
+  };
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rr = lr + 32 * i, gr = r0 + rr;
+    const bool keep = gr < R && (row_mask == nullptr || row_mask[gr] != 0);
+    uint16_t v[8];
+    if (vec && gr < R && c0 + lc < C) {
+      const uint4 w = *reinterpret_cast<const uint4*>(src + size_t(gr) * C + c0 + lc);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { v[2 * e] = uint16_t(ww[e] & 0xffff); v[2 * e + 1] = uint16_t(ww[e] >> 16); }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (gr < R && c0 + lc + e < C) ? src[size_t(gr) * C + c0 + lc + e] : 0;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[rr][lc + e] = cvt(v[e], keep);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int oc = lr + 32 * i, go = c0 + oc;       // output row = source column
+    if (go >= C) continue;
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = t[lc + e][oc];
+    if (vec && r0 + lc < R) {
+      uint4 w;
+      w.x = uint32_t(v[0]) | (uint32_t(v[1]) << 16);
+      w.y = uint32_t(v[2]) | (uint32_t(v[3]) << 16);
+      w.z = uint32_t(v[4]) | (uint32_t(v[5]) << 16);
+      w.w = uint32_t(v[6]) | (uint32_t(v[7]) << 16);
+      *reinterpret_cast<uint4*>(dst + size_t(go) * R + r0 + lc) = w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (r0 + lc + e < R) dst[size_t(go) * R + r0 + lc + e] = v[e];
+    }
+  }
+}
+
+void launch_transpose(const uint16_t* src, int R, int C, uint16_t* dst, const uint8_t* row_mask, float scale,
+                      hipStream_t stream) {
+  const int vec = (R % 8 == 0 && C % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(dst) % 16 == 0) ? 1 : 0;
+  dim3 grid((C + TP - 1) / TP, (R + TP - 1) / TP);
+  hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, stream, src, R, C, dst, row_mask, scale, vec);
+}
+
+void launch_lora_down(const uint16_t* X, const uint16_t* A, int M, int K, int r, float scale, uint16_t* T,
+                      const uint8_t* row_mask, hipStream_t stream) {
+  const unsigned tiles = unsigned((M + 31) / 32) * unsigned((r + 31) / 32);
+  hipLaunchKernelGGL(lora_down_kernel, dim3(tiles), dim3(LD_WAVES * 64), 0, stream, X, A, M, K, r, scale, T,
+                     row_mask);
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -422,6 +498,14 @@ bool use_wide(int M, int N) {
   return tiles % 256 == 0 || tiles >= 1024;
 }
 
+void launch_main(const GemmParams& g, hipStream_t stream) {
+  if (g.M == 0 || g.N == 0) return;
+  if (use_wide(g.M, g.N))
+    launch_cfg<CfgWide>(g, stream);
+  else
+    launch_cfg<CfgSquare>(g, stream);
+}
+
 }  // namespace
 
 size_t gemm_workspace_bytes(int M, int N, int K, int r) {
@@ -437,10 +521,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.r > 0) {
     // workspace: T bf16 [M, r]
     uint16_t* t = static_cast<uint16_t*>(a.ws);
-    const unsigned tiles = unsigned((a.M + 31) / 32) * unsigned((a.r + 31) / 32);
-    hipLaunchKernelGGL(lora_down_kernel, dim3(tiles), dim3(LD_WAVES * 64), 0, stream,
-                       static_cast<const uint16_t*>(a.X), static_cast<const uint16_t*>(a.A), a.M, a.K, a.r, a.scale,
-                       t);
+    launch_lora_down(static_cast<const uint16_t*>(a.X), static_cast<const uint16_t*>(a.A), a.M, a.K, a.r, a.scale,
+                     t, nullptr, stream);
     tmat = t;
   }
   GemmParams g{};
@@ -454,10 +536,99 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   g.M = a.M;
   g.N = a.N;
   g.y = static_cast<uint16_t*>(a.Y);
-  if (use_wide(a.M, a.N))
-    launch_cfg<CfgWide>(g, stream);
-  else
-    launch_cfg<CfgSquare>(g, stream);
+  launch_main(g, stream);
+  return hipGetLastError();
+}
+
+// --- backward -------------------------------------------------------------------
+// With U = s diag(m) dY B:  dX = dY W + U A,  dA = U^T X,  dB = s (diag(m) dY)^T (X A^T).
+// Every product runs on the same MFMA kernel, whose operands are K-contiguous on
+// both sides ([M, k] and [N, k]); the operands that are not (W, A, B, X, U, dY,
+// T for the contractions over N and over M) are first transposed into the
+// workspace, with the row mask and the scale applied by the transposes where the
+// formula puts them.
+namespace {
+struct BwdWs {
+  uint16_t *t, *bt, *u, *wt, *at, *ut, *xt, *dyt, *tt;
+};
+BwdWs bwd_ws(void* ws, int M, int N, int K, int r) {
+  char* c = static_cast<char*>(ws);
+  BwdWs w;
+  auto take = [&](size_t elems) {
+    uint16_t* p = reinterpret_cast<uint16_t*>(c);
+    c += align256(elems * 2);
+    return p;
+  };
+  w.t = take(size_t(M) * r);
+  w.bt = take(size_t(r) * N);
+  w.u = take(size_t(M) * r);
+  w.wt = take(size_t(K) * N);
+  w.at = take(size_t(K) * r);
+  w.ut = take(size_t(r) * M);
+  w.xt = take(size_t(K) * M);
+  w.dyt = take(size_t(N) * M);
+  w.tt = take(size_t(r) * M);
+  return w;
+}
+}  // namespace
+
+size_t gemm_bwd_workspace_bytes(int M, int N, int K, int r) {
+  if (M <= 0 || N <= 0 || K <= 0 || r <= 0) return 256;
+  const size_t m = M, n = N, k = K, rr = r;
+  return align256(m * rr * 2) * 3 + align256(rr * n * 2) + align256(k * n * 2) + align256(k * rr * 2) +
+         align256(rr * m * 2) + align256(k * m * 2) + align256(n * m * 2);
+}
+
+hipError_t launch_gemm_bwd(const GemmBwdArgs& a, hipStream_t stream) {
+  if (a.M == 0) return hipSuccess;
+  const int M = a.M, N = a.N, K = a.K, r = a.r;
+  const BwdWs w = bwd_ws(a.ws, M, N, K, r);
+  const uint16_t* X = static_cast<const uint16_t*>(a.X);
+  const uint16_t* W = static_cast<const uint16_t*>(a.W);
+  const uint16_t* A = static_cast<const uint16_t*>(a.A);
+  const uint16_t* B = static_cast<const uint16_t*>(a.B);
+  const uint16_t* dY = static_cast<const uint16_t*>(a.dY);
+  // T = X A^T (unscaled, every row); U = bf16(s diag(m) dY B) through B^T
+  launch_lora_down(X, A, M, K, r, 1.0f, w.t, nullptr, stream);
+  launch_transpose(B, N, r, w.bt, nullptr, 1.0f, stream);
+  launch_lora_down(dY, w.bt, M, N, r, a.scale, w.u, a.row_mask, stream);
+  // dX = [dY | U] [W^T | A^T]^T
+  if (a.dX) {
+    launch_transpose(W, N, K, w.wt, nullptr, 1.0f, stream);
+    launch_transpose(A, r, K, w.at, nullptr, 1.0f, stream);
+    GemmParams g{};
+    g.seg[0] = Seg{dY, w.wt, N};
+    g.seg[1] = Seg{w.u, w.at, r};
+    g.nseg = 2;
+    g.M = M;
+    g.N = K;
+    g.y = static_cast<uint16_t*>(a.dX);
+    launch_main(g, stream);
+  }
+  // dA = U^T X: rows of U^T against rows of X^T, reduction over M
+  launch_transpose(w.u, M, r, w.ut, nullptr, 1.0f, stream);
+  launch_transpose(X, M, K, w.xt, nullptr, 1.0f, stream);
+  {
+    GemmParams g{};
+    g.seg[0] = Seg{w.ut, w.xt, M};
+    g.nseg = 1;
+    g.M = r;
+    g.N = K;
+    g.y = static_cast<uint16_t*>(a.dA);
+    launch_main(g, stream);
+  }
+  // dB = (diag(m) dY)^T (s T): masked rows of dY and the scale go in with the transposes
+  launch_transpose(dY, M, N, w.dyt, a.row_mask, 1.0f, stream);
+  launch_transpose(w.t, M, r, w.tt, nullptr, a.scale, stream);
+  {
+    GemmParams g{};
+    g.seg[0] = Seg{w.dyt, w.tt, M};
+    g.nseg = 1;
+    g.M = N;
+    g.N = r;
+    g.y = static_cast<uint16_t*>(a.dB);
+    launch_main(g, stream);
+  }
   return hipGetLastError();
 }
 

@@ -75,6 +75,23 @@ int tv_max_vocab(bool bf16);          // largest V one row team covers on this d
 hipError_t launch_tv(const TvArgs& a, hipStream_t stream);
 size_t gemm_workspace_bytes(int M, int N, int K, int r);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+
+struct GemmBwdArgs {
+  const void* dY;
+  const void* X;
+  const void* W;
+  const void* A;
+  const void* B;
+  const uint8_t* row_mask;
+  float scale;
+  void* dX;        // may be null
+  void* dA;
+  void* dB;
+  int M, N, K, r;
+  void* ws;
+};
+size_t gemm_bwd_workspace_bytes(int M, int N, int K, int r);
+hipError_t launch_gemm_bwd(const GemmBwdArgs& a, hipStream_t stream);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t stream);
 
 }  // namespace uno

@@ -123,3 +123,27 @@ def uno_gated_lora_linear(X, W, A, B, row_mask, scale=1.0, out=None):
                                    ptr(Y), M, N, K, r, ptr(ws), ws.numel(), stream)
     check(st, "uno_gated_lora_linear")
     return Y
+
+
+def uno_gated_lora_linear_bwd(dY, X, W, A, B, row_mask, scale=1.0, want_dx=True):
+    """(dX or None, dA, dB) of the row-gated LoRA linear for an upstream dY (see uno.h)."""
+    lib = load()
+    M, K = X.shape
+    N = W.shape[0]
+    r = A.shape[0]
+    dev = X.device
+    require(X, "X", dtype=torch.bfloat16)
+    require(dY, "dY", dtype=torch.bfloat16, shape=(M, N), device=dev)
+    require(W, "W", dtype=torch.bfloat16, shape=(N, K), device=dev)
+    require(A, "A", dtype=torch.bfloat16, shape=(r, K), device=dev)
+    require(B, "B", dtype=torch.bfloat16, shape=(N, r), device=dev)
+    require(row_mask, "row_mask", dtype=torch.uint8, shape=(M,), device=dev)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if want_dx else None
+    dA = torch.empty((r, K), dtype=torch.bfloat16, device=dev)
+    dB = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
+    stream = stream_handle(dev)
+    ws = WORKSPACES.get(dev, stream, "gemm_bwd", lib.uno_gated_lora_linear_bwd_workspace(M, N, K, r))
+    st = lib.uno_gated_lora_linear_bwd(ptr(dY), ptr(X), ptr(W), ptr(A), ptr(B), ptr(row_mask), float(scale),
+                                       ptr(dX), ptr(dA), ptr(dB), M, N, K, r, ptr(ws), ws.numel(), stream)
+    check(st, "uno_gated_lora_linear_bwd")
+    return dX, dA, dB
