@@ -429,7 +429,8 @@ def tv_benchmark(uno, workloads, dev, iters):
 
 
 def lora_bwd_benchmark(uno, workloads, dev, iters):
-    """The gated-LoRA backward (dX, dA, dB) on both Qwen-shaped projections."""
+    """The gated-LoRA backward (dX, dA, dB) on both Qwen-shaped projections, with the
+    frozen weight's transpose made once (and, for reference, made on every call)."""
     import torch
     gcfg = workloads.GEMM_CONFIGS["qwen"]
     M, r = gcfg["M"], gcfg["r"]
@@ -438,20 +439,26 @@ def lora_bwd_benchmark(uno, workloads, dev, iters):
     for gi, (name, K, N) in enumerate(gcfg["projections"]):
         X, W, A, B = (dev_tensor(a, dev) for a in workloads.gemm_inputs(M, K, N, r, tag=gi))
         G = dev_tensor(workloads.gemm_grad(M, N, tag=gi), dev)
-        fn = lambda: uno.uno_gated_lora_linear_bwd(G, X, W, A, B, mask, 1.0)
-        fn()
+        Wt = W.t().contiguous()          # the frozen weight, transposed once (setup, not timed)
+        f_w = lambda: uno.uno_gated_lora_linear_bwd(G, X, W, A, B, mask, 1.0)
+        f_wt = lambda: uno.uno_gated_lora_linear_bwd(G, X, W, A, B, mask, 1.0, W_t=Wt)
+        f_w()
+        f_wt()
         torch.cuda.synchronize()
         timer = KernelTimer()
         for _ in range(iters):
-            timer.run("b", fn)
+            timer.run("w", f_w)
+            timer.run("b", f_wt)
         torch.cuda.synchronize()
         ms = timer.avg_ms("b")
+        ms_w = timer.avg_ms("w")
         # dX = dY W + U A, U = dY B, T = X A^T, dA = U^T X, dB = dY^T T
         flops = 2.0 * M * N * K + 2.0 * M * r * K + 2.0 * M * N * r + 2.0 * M * K * r + 2.0 * r * M * K + \
             2.0 * N * M * r
         out[f"gated_lora_bwd_{name}"] = dict(avg_us=ms * 1000, flops=flops, TFLOPs=flops / (ms * 1e9),
-                                                    mfma_frac=flops / (ms * 1e9) / BF16_PEAK_TFLOPS)
-        del X, W, A, B, G
+                                                    mfma_frac=flops / (ms * 1e9) / BF16_PEAK_TFLOPS,
+                                                    avg_us_transposing_W=ms_w * 1000)
+        del X, W, A, B, G, Wt
     torch.cuda.empty_cache()
     return out
 

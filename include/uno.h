@@ -195,6 +195,9 @@ int uno_gated_lora_linear(const void* X, const void* W, const void* A, const voi
  * bf16 in, fp32 accumulation, bf16 out; X A^T is rounded to bf16 before it meets
  * dY, as U is before it meets A and X.
  *   dY : bf16 [M, N]; X, W, A, B, row_mask, scale : as for the forward
+ *   W_t : bf16 [K, N] = W^T, optional. The base weight is frozen, so a caller
+ *   can transpose it once and pass it on every step; with NULL, W is transposed
+ *   into the workspace on every call.
  *   dX : bf16 [M, K] (out, optional: NULL skips it); dA : bf16 [r, K] (out);
  *   dB : bf16 [N, r] (out); outputs must not alias inputs or each other
  *   workspace : >= uno_gated_lora_linear_bwd_workspace(M, N, K, r) bytes (it
@@ -203,8 +206,8 @@ int uno_gated_lora_linear(const void* X, const void* W, const void* A, const voi
  * 16-byte aligned (UNO_ERR_UNSUPPORTED otherwise).
  * ------------------------------------------------------------------------- */
 size_t uno_gated_lora_linear_bwd_workspace(int M, int N, int K, int r);
-int uno_gated_lora_linear_bwd(const void* dY, const void* X, const void* W, const void* A,
-                              const void* B, const uint8_t* row_mask, float scale,
+int uno_gated_lora_linear_bwd(const void* dY, const void* X, const void* W, const void* W_t,
+                              const void* A, const void* B, const uint8_t* row_mask, float scale,
                               void* dX, void* dA, void* dB, int M, int N, int K, int r,
                               void* workspace, size_t ws_bytes, void* stream);
 

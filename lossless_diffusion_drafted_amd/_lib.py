@@ -85,8 +85,8 @@ def load():
             "uno_gated_lora_linear": (_I, [_P, _P, _P, _P, _P, ctypes.c_float, _P, _I, _I, _I,
                                            _I, _P, _SZ, _P]),
             "uno_gated_lora_linear_bwd_workspace": (_SZ, [_I, _I, _I, _I]),
-            "uno_gated_lora_linear_bwd": (_I, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _I, _I,
-                                               _I, _I, _P, _SZ, _P]),
+            "uno_gated_lora_linear_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _I,
+                                               _I, _I, _I, _P, _SZ, _P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)

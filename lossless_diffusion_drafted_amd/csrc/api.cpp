@@ -242,9 +242,9 @@ size_t uno_gated_lora_linear_bwd_workspace(int M, int N, int K, int r) {
   return uno::gemm_bwd_workspace_bytes(M, N, K, r);
 }
 
-int uno_gated_lora_linear_bwd(const void* dY, const void* X, const void* W, const void* A, const void* B,
-                              const uint8_t* row_mask, float scale, void* dX, void* dA, void* dB, int M, int N,
-                              int K, int r, void* workspace, size_t ws_bytes, void* stream) {
+int uno_gated_lora_linear_bwd(const void* dY, const void* X, const void* W, const void* W_t, const void* A,
+                              const void* B, const uint8_t* row_mask, float scale, void* dX, void* dA, void* dB,
+                              int M, int N, int K, int r, void* workspace, size_t ws_bytes, void* stream) {
   const char* fn = "uno_gated_lora_linear_bwd";
   if (M < 0 || N < 1 || K < 1 || r < 1)
     return fail(UNO_ERR_INVALID_ARG, "%s: sizes M = %d, N = %d, K = %d, r = %d out of range", fn, M, N, K, r);
@@ -255,8 +255,8 @@ int uno_gated_lora_linear_bwd(const void* dY, const void* X, const void* W, cons
   if (M % 8 != 0 || N % 8 != 0 || K % 8 != 0 || r % 8 != 0)
     return fail(UNO_ERR_UNSUPPORTED, "%s: M = %d, N = %d, K = %d and r = %d must be multiples of 8", fn, M, N,
                 K, r);
-  const void* ptrs[8] = {dY, X, W, A, B, dX, dA, dB};
-  for (int i = 0; i < 8; ++i)
+  const void* ptrs[9] = {dY, X, W, A, B, dX, dA, dB, W_t};
+  for (int i = 0; i < 9; ++i)
     if (ptrs[i] && reinterpret_cast<uintptr_t>(ptrs[i]) % 16 != 0)
       return fail(UNO_ERR_UNSUPPORTED, "%s: operand %d is not 16-byte aligned", fn, i);
   const long long lim = 0x7fffffffLL;
@@ -270,6 +270,7 @@ int uno_gated_lora_linear_bwd(const void* dY, const void* X, const void* W, cons
   a.dY = dY;
   a.X = X;
   a.W = W;
+  a.Wt = W_t;
   a.A = A;
   a.B = B;
   a.row_mask = row_mask;

@@ -594,10 +594,14 @@ hipError_t launch_gemm_bwd(const GemmBwdArgs& a, hipStream_t stream) {
   launch_lora_down(dY, w.bt, M, N, r, a.scale, w.u, a.row_mask, stream);
   // dX = [dY | U] [W^T | A^T]^T
   if (a.dX) {
-    launch_transpose(W, N, K, w.wt, nullptr, 1.0f, stream);
+    const uint16_t* wt = static_cast<const uint16_t*>(a.Wt);
+    if (!wt) {
+      launch_transpose(W, N, K, w.wt, nullptr, 1.0f, stream);
+      wt = w.wt;
+    }
     launch_transpose(A, r, K, w.at, nullptr, 1.0f, stream);
     GemmParams g{};
-    g.seg[0] = Seg{dY, w.wt, N};
+    g.seg[0] = Seg{dY, wt, N};
     g.seg[1] = Seg{w.u, w.at, r};
     g.nseg = 2;
     g.M = M;

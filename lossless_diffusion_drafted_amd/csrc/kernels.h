@@ -80,6 +80,7 @@ struct GemmBwdArgs {
   const void* dY;
   const void* X;
   const void* W;
+  const void* Wt;  // W^T [K, N] or null (then W is transposed into the workspace)
   const void* A;
   const void* B;
   const uint8_t* row_mask;

@@ -125,8 +125,9 @@ def uno_gated_lora_linear(X, W, A, B, row_mask, scale=1.0, out=None):
     return Y
 
 
-def uno_gated_lora_linear_bwd(dY, X, W, A, B, row_mask, scale=1.0, want_dx=True):
-    """(dX or None, dA, dB) of the row-gated LoRA linear for an upstream dY (see uno.h)."""
+def uno_gated_lora_linear_bwd(dY, X, W, A, B, row_mask, scale=1.0, want_dx=True, W_t=None):
+    """(dX or None, dA, dB) of the row-gated LoRA linear for an upstream dY (see uno.h).
+    W_t, optional, is W^T [K, N] made once by the caller (the base weight is frozen)."""
     lib = load()
     M, K = X.shape
     N = W.shape[0]
@@ -138,12 +139,14 @@ def uno_gated_lora_linear_bwd(dY, X, W, A, B, row_mask, scale=1.0, want_dx=True)
     require(A, "A", dtype=torch.bfloat16, shape=(r, K), device=dev)
     require(B, "B", dtype=torch.bfloat16, shape=(N, r), device=dev)
     require(row_mask, "row_mask", dtype=torch.uint8, shape=(M,), device=dev)
+    if W_t is not None:
+        require(W_t, "W_t", dtype=torch.bfloat16, shape=(K, N), device=dev)
     dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if want_dx else None
     dA = torch.empty((r, K), dtype=torch.bfloat16, device=dev)
     dB = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
     stream = stream_handle(dev)
     ws = WORKSPACES.get(dev, stream, "gemm_bwd", lib.uno_gated_lora_linear_bwd_workspace(M, N, K, r))
-    st = lib.uno_gated_lora_linear_bwd(ptr(dY), ptr(X), ptr(W), ptr(A), ptr(B), ptr(row_mask), float(scale),
+    st = lib.uno_gated_lora_linear_bwd(ptr(dY), ptr(X), ptr(W), ptr(W_t), ptr(A), ptr(B), ptr(row_mask), float(scale),
                                        ptr(dX), ptr(dA), ptr(dB), M, N, K, r, ptr(ws), ws.numel(), stream)
     check(st, "uno_gated_lora_linear_bwd")
     return dX, dA, dB

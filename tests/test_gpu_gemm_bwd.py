@@ -130,3 +130,17 @@ def test_backward_argument_errors():
     with pytest.raises(uno.UnoError) as e:
         uno.uno_gated_lora_linear_bwd(z(12, 16), z(12, 16), z(16, 16), z(8, 16), z(16, 8), m, 1.0)
     assert e.value.status == "UNO_ERR_UNSUPPORTED"      # M = 12 is not a multiple of 8
+
+
+def test_backward_with_pretransposed_weight():
+    """Passing W^T gives the same bits as transposing W inside the call."""
+    M, K, N, r = 256, 768, 512, 32
+    X, W, A, B = workloads.gemm_inputs(M, K, N, r, seed=12)
+    G = workloads.gemm_grad(M, N, seed=12)
+    args = [to_device(a, DEV) for a in (G, X, W, A, B)]
+    mask = to_device(workloads.noise_row_mask(M // 8, 8), DEV)
+    a = _uno().uno_gated_lora_linear_bwd(*args, mask, 4.0)
+    b = _uno().uno_gated_lora_linear_bwd(*args, mask, 4.0, W_t=args[2].t().contiguous())
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
