@@ -38,6 +38,9 @@ constexpr int VT = 256;               // threads per workgroup
 constexpr int VW = VT / kWave;        // waves per workgroup
 constexpr int UNR = 8;                // 16-byte loads per thread per tile
 constexpr int CAND_CAP = 1024;        // candidates kept per row
+constexpr int WAVE_CHUNKS = 128;      // 16-byte chunks each wave may flag in its own list
+constexpr int SPILL_CHUNKS = 153;     // shared by the waves whose own list is full
+constexpr int CHUNK_CAP = VT / 64 * WAVE_CHUNKS + SPILL_CHUNKS;   // chunks a row may flag
 constexpr int WAVE_SEL_MAX = 512;     // candidates one wave selects from (8 per lane)
 constexpr int SEL_CAP = 256;          // largest filtered support on this path
 constexpr int KMAX_FAST = 256;          // largest top-k the stream bound is built for
@@ -59,14 +62,28 @@ struct Dist {            // filtered distribution: ascending ids, fp64 probabili
 };
 
 struct RowLds {          // per-row state of the selection
-  float cval[CAND_CAP];
-  int cidx[CAND_CAP];
-  alignas(16) float sval[SEL_CAP];
-  alignas(16) int sidx[SEL_CAP];
-  double sw[SEL_CAP];
-  unsigned hist[256];
+  union {
+    // During the stream: the flagged chunks (raw 16 bytes and the element index
+    // of their first entry); wave w's own list at [w * WAVE_CHUNKS, ...), the
+    // shared spill area after the four lists.
+    struct {
+      uint4 cdata[CHUNK_CAP];
+      int cpos[CHUNK_CAP];
+    };
+    // After the stream: the candidate list and the selection's work arrays.
+    struct {
+      float cval[CAND_CAP];
+      int cidx[CAND_CAP];
+      alignas(16) float sval[SEL_CAP];
+      alignas(16) int sidx[SEL_CAP];
+      double sw[SEL_CAP];
+      unsigned hist[256];
+    };
+  };
   float wthr[VW];        // per-wave published lower bounds
-  int cnt;               // candidates pushed (may exceed CAND_CAP: overflow)
+  int wchunk[VW];        // chunks in each wave's own list
+  int nspill;            // chunks sent to the spill area (may exceed SPILL_CHUNKS: overflow)
+  int cnt;               // candidates kept; > CAND_CAP marks an overflow
   int n;                 // size of the tie-inclusive top-k set
   unsigned kmax;         // largest candidate key
   int status;
@@ -182,6 +199,7 @@ struct RowScan {
   float thr;        // current lower bound of the k-th largest value
   float lmax;       // running maximum of this lane's elements (float path)
   int lmax16;       // running maximum as a signed 16-bit bf16 pattern (packed path)
+  int nchunk;       // chunks in this wave's own list (wave-uniform)
 };
 
 // c-th largest of the wave's 64 lane values (LDS broadcast reads; a wave's LDS
@@ -204,7 +222,7 @@ __device__ __forceinline__ void process_tile(const RowView<E, VEC>& rv, RowLds& 
                                              int t, RowScan& sc) {
   using EL = Elem<E>;
   constexpr int VN = EL::VN;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wid = tid / kWave;
   const int V = rv.V;
   const float thr = sc.thr;
   const bool tail = t >= rv.full_tiles;
@@ -238,15 +256,26 @@ __device__ __forceinline__ void process_tile(const RowView<E, VEC>& rv, RowLds& 
       sc.lmax = fmaxf(sc.lmax, mx);
       maybe = mx >= thr;
     }
-    if (maybe) {
-      float x[VN];
-      EL::unpack(r[u], x);
-#pragma unroll
-      for (int j = 0; j < VN; ++j) {
-        if (x[j] >= thr && e0 + j < V) {
-          const int p = atomicAdd(&R.cnt, 1);
-          if (p < CAND_CAP) { R.cval[p] = x[j]; R.cidx[p] = e0 + j; }
-        }
+    // A chunk that may hold an element at or above the bound is kept whole; its
+    // elements are tested against the final bound once the row is read. Slots
+    // come from the ballot ranks in the wave's own list (a wave-uniform count, no
+    // atomic), or, once that list is full, from the shared spill area.
+    const unsigned long long bal = __ballot(maybe);
+    if (bal) {
+      const int n = __popcll(bal), rank = ballot_rank(bal);
+      int pos;
+      if (sc.nchunk + n <= WAVE_CHUNKS) {
+        pos = wid * WAVE_CHUNKS + sc.nchunk + rank;
+        sc.nchunk += n;
+      } else {
+        int base = 0;
+        if ((tid & (kWave - 1)) == 0) base = atomicAdd(&R.nspill, n);
+        const int sp = readlane_i(base, 0) + rank;
+        pos = sp < SPILL_CHUNKS ? VW * WAVE_CHUNKS + sp : CHUNK_CAP;
+      }
+      if (maybe && pos < CHUNK_CAP) {
+        R.cdata[pos] = r[u];
+        R.cpos[pos] = e0;
       }
     }
   }
@@ -296,7 +325,95 @@ __device__ __forceinline__ float read_bound(const RowLds& R) {
 }
 
 __device__ __forceinline__ void reset_row(RowLds& R) {
-  if (threadIdx.x == 0) { R.cnt = 0; R.status = ROW_OK; R.n = 0; }
+  if (threadIdx.x == 0) { R.nspill = 0; R.cnt = 0; R.status = ROW_OK; R.n = 0; }
+}
+
+// This wave's lane-maximum bound after the whole row and its chunk count
+// (published; caller synchronises). The bound is -inf when the stream runs
+// unbounded.
+__device__ __forceinline__ void publish_row_end(RowLds& R, const RowScan& sc, bool bounded, int c, Shared& sh) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const float tw = bounded ? wave_cth_largest(scan_lane_max(sc), c, sh) : -INFINITY;
+  if (lane == 0) {
+    R.wthr[wid] = tw;
+    R.wchunk[wid] = sc.nchunk;
+  }
+}
+
+// Chunks this thread holds of the row's list: entry m * VT + threadIdx.x.
+constexpr int CHUNKS_PER_THREAD = (CHUNK_CAP + VT - 1) / VT;
+struct HeldChunks {
+  uint4 d[CHUNKS_PER_THREAD];
+  int pos[CHUNKS_PER_THREAD];
+  int n;                // valid entries of the list
+  bool overflow;
+};
+
+// Entry e of the row's list in the order: wave 0's list, ..., wave 3's, spill.
+__device__ __forceinline__ void take_chunks(const RowLds& R, HeldChunks& h) {
+  int start[VW + 1], off[VW + 1];
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < VW; ++w) {
+    start[w] = total;
+    off[w] = w * WAVE_CHUNKS;
+    total += R.wchunk[w];
+  }
+  const int ns = R.nspill;
+  start[VW] = total;
+  off[VW] = VW * WAVE_CHUNKS;
+  h.overflow = ns > SPILL_CHUNKS;
+  total += min(ns, SPILL_CHUNKS);
+  h.n = total;
+#pragma unroll
+  for (int m = 0; m < CHUNKS_PER_THREAD; ++m) {
+    const int e = m * VT + int(threadIdx.x);
+    if (e < total) {
+      int seg = 0;
+#pragma unroll
+      for (int w = 1; w <= VW; ++w) seg = e >= start[w] ? w : seg;
+      int src = e - start[0] + off[0];
+#pragma unroll
+      for (int w = 1; w <= VW; ++w) src = seg == w ? e - start[w] + off[w] : src;
+      h.d[m] = R.cdata[src];
+      h.pos[m] = R.cpos[src];
+    }
+  }
+}
+
+// The held chunks' elements at or above `thr` become the row's candidate list
+// (cval/cidx, count in cnt). An overflowed chunk list makes cnt exceed CAND_CAP,
+// which sends the row to the full-row path.
+template <typename E>
+__device__ __forceinline__ void expand_chunks(RowLds& R, const HeldChunks& h, float thr, int V) {
+  using EL = Elem<E>;
+  constexpr int VN = EL::VN;
+  int cnt = 0;
+#pragma unroll
+  for (int m = 0; m < CHUNKS_PER_THREAD; ++m) {
+    if (m * VT + int(threadIdx.x) < h.n) {
+      float x[VN];
+      EL::unpack(h.d[m], x);
+#pragma unroll
+      for (int j = 0; j < VN; ++j) cnt += (x[j] >= thr && h.pos[m] + j < V) ? 1 : 0;
+    }
+  }
+  int p = cnt ? atomicAdd(&R.cnt, cnt) : 0;
+#pragma unroll
+  for (int m = 0; m < CHUNKS_PER_THREAD; ++m) {
+    if (m * VT + int(threadIdx.x) < h.n) {
+      float x[VN];
+      EL::unpack(h.d[m], x);
+#pragma unroll
+      for (int j = 0; j < VN; ++j) {
+        if (x[j] >= thr && h.pos[m] + j < V) {
+          if (p < CAND_CAP) { R.cval[p] = x[j]; R.cidx[p] = h.pos[m] + j; }
+          ++p;
+        }
+      }
+    }
+  }
+  if (threadIdx.x == 0 && h.overflow) atomicAdd(&R.cnt, CAND_CAP + 1);
 }
 
 // Stream one row (scalar path, or a row without a partner) with double buffering
@@ -310,7 +427,7 @@ __device__ __forceinline__ void stream_one(const RowView<E, VEC>& rv, const Filt
   uint4 A[UNR], B[UNR];
   rv.load_tile(A, 0);
   if (VEC || rv.ntiles > 1) rv.load_tile(B, 1);
-  RowScan sc{-INFINITY, -INFINITY, -32768};
+  RowScan sc{-INFINITY, -INFINITY, -32768, 0};
   if (bounded) init_bound(rv, R, A, c, sc, sh);
   __syncthreads();
   if (bounded) sc.thr = read_bound(R);
@@ -333,6 +450,12 @@ __device__ __forceinline__ void stream_one(const RowView<E, VEC>& rv, const Filt
       }
     }
   }
+  publish_row_end(R, sc, bounded, c, sh);
+  HeldChunks h;
+  __syncthreads();                    // every chunk flagged; bounds and counts published
+  take_chunks(R, h);
+  __syncthreads();                    // the list read before its arrays are reused
+  expand_chunks<E>(R, h, bounded ? read_bound(R) : -INFINITY, rv.V);
   __syncthreads();
 }
 
@@ -346,7 +469,7 @@ __device__ __forceinline__ void stream_two(const RowView<E, true>& pv, const Row
   uint4 A[UNR], B[UNR];
   pv.load_tile(A, 0);
   qv.load_tile(B, 0);
-  RowScan sp{-INFINITY, -INFINITY, -32768}, sq{-INFINITY, -INFINITY, -32768};
+  RowScan sp{-INFINITY, -INFINITY, -32768, 0}, sq{-INFINITY, -INFINITY, -32768, 0};
   if (bounded) {
     init_bound(pv, Rp, A, c, sp, sh);
     init_bound(qv, Rq, B, c, sq, sh);
@@ -367,6 +490,21 @@ __device__ __forceinline__ void stream_two(const RowView<E, true>& pv, const Row
       sp.thr = refresh_bound(Rp, sp, c, sh);
       sq.thr = refresh_bound(Rq, sq, c, sh);
     }
+  }
+  publish_row_end(Rp, sp, bounded, c, sh);
+  publish_row_end(Rq, sq, bounded, c, sh);
+  __syncthreads();                    // every chunk flagged; bounds and counts published
+  {
+    HeldChunks h;
+    take_chunks(Rp, h);
+    __syncthreads();                  // p's list read before its arrays are reused
+    expand_chunks<E>(Rp, h, bounded ? read_bound(Rp) : -INFINITY, pv.V);
+  }
+  {
+    HeldChunks h;
+    take_chunks(Rq, h);
+    __syncthreads();                  // the same for q
+    expand_chunks<E>(Rq, h, bounded ? read_bound(Rq) : -INFINITY, qv.V);
   }
   __syncthreads();
 }
@@ -1231,7 +1369,8 @@ __device__ __forceinline__ SlotResult full_slot(const RowView<E, VEC>& pv, const
 }
 
 template <typename E, bool VEC>
-__global__ __launch_bounds__(VT) void verify_kernel(VerifyArgs a) {
+// Four workgroups per CU keep every slot of a 64 x 16 block resident at once.
+__global__ __launch_bounds__(VT) __attribute__((amdgpu_waves_per_eu(4))) void verify_kernel(VerifyArgs a) {
   __shared__ Shared sh;
   const int g = xcd_contiguous_id(blockIdx.x, gridDim.x);
   const int b = a.b, V = a.V;
