@@ -92,7 +92,6 @@ struct RowLds {          // per-row state of the selection
 struct Shared {
   RowLds row[2];         // 0: base row p, 1: draft row q
   Dist dist[2];
-  alignas(16) float lanebuf[VW][kWave];
   unsigned red_u[VW][3];
   unsigned ures[2];
 };
@@ -124,6 +123,7 @@ __device__ __forceinline__ int ballot_rank(unsigned long long mask) {
 template <typename E> struct Elem;
 template <> struct Elem<uint16_t> {        // bf16 bit patterns
   static constexpr int VN = 8;
+  static constexpr int KEY_BITS = 16;      // significant bits of an element's order key
   __device__ static void unpack(const uint4& r, float* x) {
     x[0] = bf16_lo(r.x); x[1] = bf16_hi(r.x); x[2] = bf16_lo(r.y); x[3] = bf16_hi(r.y);
     x[4] = bf16_lo(r.z); x[5] = bf16_hi(r.z); x[6] = bf16_lo(r.w); x[7] = bf16_hi(r.w);
@@ -143,6 +143,7 @@ template <> struct Elem<uint16_t> {        // bf16 bit patterns
 };
 template <> struct Elem<float> {
   static constexpr int VN = 4;
+  static constexpr int KEY_BITS = 32;
   __device__ static void unpack(const uint4& r, float* x) {
     x[0] = __uint_as_float(r.x); x[1] = __uint_as_float(r.y);
     x[2] = __uint_as_float(r.z); x[3] = __uint_as_float(r.w);
@@ -202,19 +203,27 @@ struct RowScan {
   int nchunk;       // chunks in this wave's own list (wave-uniform)
 };
 
-// c-th largest of the wave's 64 lane values (LDS broadcast reads; a wave's LDS
-// operations complete in order, so no barrier is needed).
-__device__ __forceinline__ float wave_cth_largest(float m, int c, Shared& sh) {
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  sh.lanebuf[wid][lane] = m;
-  const float4* lb = reinterpret_cast<const float4*>(sh.lanebuf[wid]);
-  int cnt_ge = 0;
-#pragma unroll
-  for (int j = 0; j < kWave / 4; ++j) {
-    const float4 v = lb[j];
-    cnt_ge += (v.x >= m) + (v.y >= m) + (v.z >= m) + (v.w >= m);
+// The c-th largest of the wave's 64 lane values: an MSB-first radix select over
+// the top `bits` bits of the order keys, one ballot per bit (no LDS). Exact for
+// bf16 values with bits = 16 and for any float with bits = 32. NaN lanes count
+// as -inf.
+__device__ __forceinline__ float wave_cth_largest(float m, int c, int bits) {
+  const int drop = 32 - bits;
+  const uint32_t key = float_key(m == m ? m : -INFINITY) >> drop;
+  uint32_t prefix = 0u, decided = 0u;
+  int need = c;
+  for (int b = bits - 1; b >= 0; --b) {
+    const uint32_t bit = 1u << b;
+    const bool one = ((key ^ prefix) & decided) == 0u && (key & bit) != 0u;
+    const int n1 = __popcll(__ballot(one));
+    if (n1 >= need) prefix |= bit;
+    else need -= n1;
+    decided |= bit;
   }
-  return wave_max(cnt_ge >= c ? m : -INFINITY);
+  // Below zero the dropped key bits are ones (the key of a negative float is
+  // its complement), so they are restored as ones.
+  const uint32_t low = ((prefix >> (bits - 1)) & 1u) ? 0u : ((1u << drop) - 1u);
+  return key_float((prefix << drop) | low);
 }
 
 template <typename E, bool VEC>
@@ -288,9 +297,9 @@ __device__ __forceinline__ float scan_lane_max(const RowScan& sc) {
 }
 
 // Publish this wave's bound for row R and return the current minimum over waves.
-__device__ __forceinline__ float refresh_bound(RowLds& R, const RowScan& sc, int c, Shared& sh) {
+__device__ __forceinline__ float refresh_bound(RowLds& R, const RowScan& sc, int c, int bits) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  const float tw = wave_cth_largest(scan_lane_max(sc), c, sh);
+  const float tw = wave_cth_largest(scan_lane_max(sc), c, bits);
   if (lane == 0) R.wthr[wid] = tw;
   float t = R.wthr[0];
 #pragma unroll
@@ -301,7 +310,7 @@ __device__ __forceinline__ float refresh_bound(RowLds& R, const RowScan& sc, int
 // First-tile lane maxima -> initial bound (published; caller synchronises).
 template <typename E, bool VEC>
 __device__ __forceinline__ void init_bound(const RowView<E, VEC>& rv, RowLds& R, const uint4 (&r)[UNR],
-                                           int c, RowScan& sc, Shared& sh) {
+                                           int c, RowScan& sc) {
   using EL = Elem<E>;
   constexpr int VN = EL::VN;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
@@ -313,7 +322,7 @@ __device__ __forceinline__ void init_bound(const RowView<E, VEC>& rv, RowLds& R,
 #pragma unroll
     for (int j = 0; j < VN; ++j) sc.lmax = (e0 + j < rv.V) ? fmaxf(sc.lmax, x[j]) : sc.lmax;
   }
-  const float tw = wave_cth_largest(sc.lmax, c, sh);
+  const float tw = wave_cth_largest(sc.lmax, c, EL::KEY_BITS);
   if (lane == 0) R.wthr[wid] = tw;
 }
 
@@ -331,9 +340,9 @@ __device__ __forceinline__ void reset_row(RowLds& R) {
 // This wave's lane-maximum bound after the whole row and its chunk count
 // (published; caller synchronises). The bound is -inf when the stream runs
 // unbounded.
-__device__ __forceinline__ void publish_row_end(RowLds& R, const RowScan& sc, bool bounded, int c, Shared& sh) {
+__device__ __forceinline__ void publish_row_end(RowLds& R, const RowScan& sc, bool bounded, int c, int bits) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  const float tw = bounded ? wave_cth_largest(scan_lane_max(sc), c, sh) : -INFINITY;
+  const float tw = bounded ? wave_cth_largest(scan_lane_max(sc), c, bits) : -INFINITY;
   if (lane == 0) {
     R.wthr[wid] = tw;
     R.wchunk[wid] = sc.nchunk;
@@ -428,16 +437,20 @@ __device__ __forceinline__ void stream_one(const RowView<E, VEC>& rv, const Filt
   rv.load_tile(A, 0);
   if (VEC || rv.ntiles > 1) rv.load_tile(B, 1);
   RowScan sc{-INFINITY, -INFINITY, -32768, 0};
-  if (bounded) init_bound(rv, R, A, c, sc, sh);
+  constexpr int KB = Elem<E>::KEY_BITS;
+  if (bounded) init_bound(rv, R, A, c, sc);
   __syncthreads();
   if (bounded) sc.thr = read_bound(R);
   if (VEC) {
+    // The bound rises fastest early on, when each tile adds many lane maxima:
+    // it is refreshed after each of the first eight tiles.
     for (int t = 0; t < rv.ntiles; t += 2) {
       process_tile(rv, R, A, t, sc);
       rv.load_tile(A, t + 2);
+      if (bounded && t < 8) sc.thr = refresh_bound(R, sc, c, KB);
       if (t + 1 < rv.ntiles) process_tile(rv, R, B, t + 1, sc);
       rv.load_tile(B, t + 3);
-      if (bounded && (t == 0 || t == 2 || t == 6)) sc.thr = refresh_bound(R, sc, c, sh);
+      if (bounded && t < 8) sc.thr = refresh_bound(R, sc, c, KB);
     }
   } else {
     process_tile(rv, R, A, 0, sc);
@@ -450,13 +463,25 @@ __device__ __forceinline__ void stream_one(const RowView<E, VEC>& rv, const Filt
       }
     }
   }
-  publish_row_end(R, sc, bounded, c, sh);
+  publish_row_end(R, sc, bounded, c, KB);
   HeldChunks h;
   __syncthreads();                    // every chunk flagged; bounds and counts published
   take_chunks(R, h);
   __syncthreads();                    // the list read before its arrays are reused
   expand_chunks<E>(R, h, bounded ? read_bound(R) : -INFINITY, rv.V);
   __syncthreads();
+}
+
+// Issue priority of this wave (0..3). Waves further along a row step down so
+// that the workgroups sharing a CU finish their streams together instead of in
+// start order.
+__device__ __forceinline__ void set_wave_prio(int p) {
+  switch (p) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+  }
 }
 
 // Stream two rows of the same length interleaved tile by tile (vector path).
@@ -470,16 +495,20 @@ __device__ __forceinline__ void stream_two(const RowView<E, true>& pv, const Row
   pv.load_tile(A, 0);
   qv.load_tile(B, 0);
   RowScan sp{-INFINITY, -INFINITY, -32768, 0}, sq{-INFINITY, -INFINITY, -32768, 0};
+  constexpr int KB = Elem<E>::KEY_BITS;
   if (bounded) {
-    init_bound(pv, Rp, A, c, sp, sh);
-    init_bound(qv, Rq, B, c, sq, sh);
+    init_bound(pv, Rp, A, c, sp);
+    init_bound(qv, Rq, B, c, sq);
   }
   __syncthreads();
   if (bounded) {
     sp.thr = read_bound(Rp);
     sq.thr = read_bound(Rq);
   }
+  int prio = -1;
   for (int t = 0; t < pv.ntiles; ++t) {
+    const int want = 3 - (t * 4) / pv.ntiles;
+    if (want != prio) { set_wave_prio(want); prio = want; }
     process_tile(pv, Rp, A, t, sp);
     pv.load_tile(A, t + 1);
     process_tile(qv, Rq, B, t, sq);
@@ -487,12 +516,13 @@ __device__ __forceinline__ void stream_two(const RowView<E, true>& pv, const Row
     // The bound rises fastest early on, when each tile adds many lane maxima:
     // refreshing it after each of the first 8 tiles keeps fewer candidates.
     if (bounded && t < 8) {
-      sp.thr = refresh_bound(Rp, sp, c, sh);
-      sq.thr = refresh_bound(Rq, sq, c, sh);
+      sp.thr = refresh_bound(Rp, sp, c, KB);
+      sq.thr = refresh_bound(Rq, sq, c, KB);
     }
   }
-  publish_row_end(Rp, sp, bounded, c, sh);
-  publish_row_end(Rq, sq, bounded, c, sh);
+  set_wave_prio(0);
+  publish_row_end(Rp, sp, bounded, c, KB);
+  publish_row_end(Rq, sq, bounded, c, KB);
   __syncthreads();                    // every chunk flagged; bounds and counts published
   {
     HeldChunks h;
