@@ -95,6 +95,41 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
   return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
+// Cross-lane moves within each row of 16 lanes (DPP, no LDS): XOR 1 and XOR 2
+// inside each quad, mirror within each half-row and within the row. Applied in
+// that order to a commutative reduction they leave the row's result in every
+// lane of the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+// Sum / maximum over the 8 lanes of each half-row (lanes 0-7 hold the result
+// for lanes 0-7).
+__device__ __forceinline__ float lanes8_sum(float v) {
+  v += dpp_f<kDppQuadXor1>(v);
+  v += dpp_f<kDppQuadXor2>(v);
+  return v + dpp_f<kDppHalfMirror>(v);
+}
+__device__ __forceinline__ float lanes8_max(float v) {
+  v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+  return fmaxf(v, dpp_f<kDppHalfMirror>(v));
+}
+// Wave64 sum / maximum without LDS: row reductions by DPP, then the four row
+// results read from lanes 0, 16, 32, 48 (the same order in every lane).
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = lanes8_sum(v);
+  v += dpp_f<kDppMirror>(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = lanes8_max(v);
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+
 // Inclusive prefix sum over lanes 0..63.
 template <typename T>
 __device__ __forceinline__ T wave_inclusive_scan(T v) {

@@ -64,7 +64,6 @@ constexpr size_t kRowOff = kRecOff + size_t(kMaxWg) * 64;
 struct TvLds {
   float wred[TWAVES][4];
   float rec[64][4];
-  float norm[4];
   int ok;
   int last;
 };
@@ -390,46 +389,49 @@ __global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       zt += et[j];
       zs += es[j];
     }
-    // Wave partials, then workgroup partial by thread 0 (fp64), then the team.
+    // Wave partials (DPP reductions), then the workgroup partial over the eight
+    // waves in lanes 0-7 of wave 0, then the team.
     {
-      const float wmt = wave_max(zt > 0.0f ? mt : -INFINITY);
-      const float wms = wave_max(zs > 0.0f ? ms : -INFINITY);
+      const float wmt = wave_max_dpp(zt > 0.0f ? mt : -INFINITY);
+      const float wms = wave_max_dpp(zs > 0.0f ? ms : -INFINITY);
       const float st = zt > 0.0f ? zt * __builtin_amdgcn_exp2f((mt - wmt) * c) : 0.0f;
       const float ss = zs > 0.0f ? zs * __builtin_amdgcn_exp2f((ms - wms) * c) : 0.0f;
-      const float wzt = wave_sum(st), wzs = wave_sum(ss);
+      const float wzt = wave_sum_dpp(st), wzs = wave_sum_dpp(ss);
       if (lane == 0) { sh.wred[wid][0] = wmt; sh.wred[wid][1] = wzt; sh.wred[wid][2] = wms; sh.wred[wid][3] = wzs; }
       __syncthreads();
-      if (tid == 0) {
-        float Mt = -INFINITY, Ms = -INFINITY;
-        double Zt = 0.0, Zs = 0.0;
-        for (int w = 0; w < TWAVES; ++w) { Mt = fmaxf(Mt, sh.wred[w][0]); Ms = fmaxf(Ms, sh.wred[w][2]); }
-        for (int w = 0; w < TWAVES; ++w) {
-          if (sh.wred[w][1] > 0.0f) Zt += double(sh.wred[w][1] * __builtin_amdgcn_exp2f((sh.wred[w][0] - Mt) * c));
-          if (sh.wred[w][3] > 0.0f) Zs += double(sh.wred[w][3] * __builtin_amdgcn_exp2f((sh.wred[w][2] - Ms) * c));
+      if (wid == 0) {
+        const bool in = lane < TWAVES;
+        const float m0 = in ? sh.wred[lane][0] : -INFINITY, z0 = in ? sh.wred[lane][1] : 0.0f;
+        const float m1 = in ? sh.wred[lane][2] : -INFINITY, z1 = in ? sh.wred[lane][3] : 0.0f;
+        const float Mt = lanes8_max(z0 > 0.0f ? m0 : -INFINITY);
+        const float Ms = lanes8_max(z1 > 0.0f ? m1 : -INFINITY);
+        const float Zt = lanes8_sum(z0 > 0.0f ? z0 * __builtin_amdgcn_exp2f((m0 - Mt) * c) : 0.0f);
+        const float Zs = lanes8_sum(z1 > 0.0f ? z1 * __builtin_amdgcn_exp2f((m1 - Ms) * c) : 0.0f);
+        if (lane == 0) {
+          const float v[4] = {Mt, Zt, Ms, Zs};
+          publish(my_rec, v, 4, epoch_tag | ((nbar + 1) & 0xffffu));
         }
-        const float v[4] = {Mt, float(Zt), Ms, float(Zs)};
-        publish(my_rec, v, 4, epoch_tag | ((nbar + 1) & 0xffffu));
       }
     }
     ++nbar;
     if (!gather(team_rec, G, 0, 4, epoch_tag | (nbar & 0xffffu), &hdr->abort, sh)) { ok = false; break; }
-    if (tid == 0) {
-      float Mt = -INFINITY, Ms = -INFINITY;
-      double Zt = 0.0, Zs = 0.0;
-      for (int j = 0; j < G; ++j) { Mt = fmaxf(Mt, sh.rec[j][0]); Ms = fmaxf(Ms, sh.rec[j][2]); }
-      for (int j = 0; j < G; ++j) {
-        if (sh.rec[j][1] > 0.0f) Zt += double(sh.rec[j][1]) * double(__builtin_amdgcn_exp2f((sh.rec[j][0] - Mt) * c));
-        if (sh.rec[j][3] > 0.0f) Zs += double(sh.rec[j][3]) * double(__builtin_amdgcn_exp2f((sh.rec[j][2] - Ms) * c));
-      }
-      sh.norm[0] = Mt;
-      sh.norm[1] = float(log2(Zt));
-      sh.norm[2] = Ms;
-      sh.norm[3] = float(log2(Zs));
+    // Team normalisers, computed by every wave from the gathered records (member
+    // j in lane j; G <= 64): maxima, then the sums of the rescaled partials.
+    float Mt, Ms, lzt, lzs;
+    {
+      const bool in = lane < G;
+      const float m0 = in ? sh.rec[lane][0] : -INFINITY, z0 = in ? sh.rec[lane][1] : 0.0f;
+      const float m1 = in ? sh.rec[lane][2] : -INFINITY, z1 = in ? sh.rec[lane][3] : 0.0f;
+      Mt = wave_max_dpp(z0 > 0.0f ? m0 : -INFINITY);
+      Ms = wave_max_dpp(z1 > 0.0f ? m1 : -INFINITY);
+      const float Zt = wave_sum_dpp(z0 > 0.0f ? z0 * __builtin_amdgcn_exp2f((m0 - Mt) * c) : 0.0f);
+      const float Zs = wave_sum_dpp(z1 > 0.0f ? z1 * __builtin_amdgcn_exp2f((m1 - Ms) * c) : 0.0f);
+      lzt = __builtin_amdgcn_logf(Zt);
+      lzs = __builtin_amdgcn_logf(Zs);
     }
-    __syncthreads();
     // p = et * at, q = es * as: exp2 of the thread-max offset minus log2 Z.
-    const float at = __builtin_amdgcn_exp2f((mt - sh.norm[0]) * c - sh.norm[1]);
-    const float as = __builtin_amdgcn_exp2f((ms - sh.norm[2]) * c - sh.norm[3]);
+    const float at = __builtin_amdgcn_exp2f((mt - Mt) * c - lzt);
+    const float as = __builtin_amdgcn_exp2f((ms - Ms) * c - lzs);
     // ---- pass 2: |q - p| and q sign(q - p); keep (sign, q) ----
     float tvs = 0.0f, gs = 0.0f;
 #pragma unroll
@@ -448,14 +450,17 @@ __global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     }
     __syncthreads();                           // sh.rec / sh.wred reuse
     {
-      const float wt = wave_sum(tvs), wg = wave_sum(gs);
+      const float wt = wave_sum_dpp(tvs), wg = wave_sum_dpp(gs);
       if (lane == 0) { sh.wred[wid][0] = wt; sh.wred[wid][1] = wg; }
       __syncthreads();
-      if (tid == 0) {
-        double T = 0.0, Gs = 0.0;
-        for (int w = 0; w < TWAVES; ++w) { T += double(sh.wred[w][0]); Gs += double(sh.wred[w][1]); }
-        const float v[2] = {float(T), float(Gs)};
-        publish(my_rec + 4, v, 2, epoch_tag | ((nbar + 1) & 0xffffu));
+      if (wid == 0) {
+        const bool in = lane < TWAVES;
+        const float T = lanes8_sum(in ? sh.wred[lane][0] : 0.0f);
+        const float Gs = lanes8_sum(in ? sh.wred[lane][1] : 0.0f);
+        if (lane == 0) {
+          const float v[2] = {T, Gs};
+          publish(my_rec + 4, v, 2, epoch_tag | ((nbar + 1) & 0xffffu));
+        }
       }
     }
     ++nbar;
