@@ -59,29 +59,63 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 }
 
 // ---------------------------------------------------------------------------
-// Wave64 reductions and scans (lane shuffles; every lane gets the result).
+// Wave64 reductions (every lane gets the result). Row steps move values with DPP
+// (no LDS): XOR 1 and XOR 2 inside each quad, then the mirror within each
+// half-row and within the row; applied in that order to a commutative operation
+// they leave the row's result in every lane of the row. The four row results are
+// then read from lanes 0, 16, 32 and 48 and combined in that order, the same in
+// every lane.
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_move(T v) {
+  if constexpr (sizeof(T) == 8) {
+    const long long b = __builtin_bit_cast(long long, v);
+    const unsigned lo = unsigned(dpp_i<CTRL>(int(b & 0xffffffffll)));
+    const unsigned hi = unsigned(dpp_i<CTRL>(int(b >> 32)));
+    return __builtin_bit_cast(T, (long long)(((unsigned long long)hi << 32) | lo));
+  } else {
+    return __builtin_bit_cast(T, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+  }
+}
+template <typename T>
+__device__ __forceinline__ T lane_read(T v, int l) {
+  if constexpr (sizeof(T) == 8) {
+    const long long b = __builtin_bit_cast(long long, v);
+    const unsigned lo = unsigned(__builtin_amdgcn_readlane(int(b & 0xffffffffll), l));
+    const unsigned hi = unsigned(__builtin_amdgcn_readlane(int(b >> 32), l));
+    return __builtin_bit_cast(T, (long long)(((unsigned long long)hi << 32) | lo));
+  } else {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+  }
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  v = op(v, dpp_move<kDppQuadXor1>(v));
+  v = op(v, dpp_move<kDppQuadXor2>(v));
+  v = op(v, dpp_move<kDppHalfMirror>(v));
+  v = op(v, dpp_move<kDppMirror>(v));
+  return op(op(lane_read(v, 0), lane_read(v, 16)), op(lane_read(v, 32), lane_read(v, 48)));
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, [](T a, T b) { return a + b; });
 }
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) { T w = __shfl_xor(v, o, kWave); v = w > v ? w : v; }
-  return v;
+  return wave_reduce(v, [](T a, T b) { return b > a ? b : a; });
 }
 template <typename T>
 __device__ __forceinline__ T wave_min(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) { T w = __shfl_xor(v, o, kWave); v = w < v ? w : v; }
-  return v;
+  return wave_reduce(v, [](T a, T b) { return b < a ? b : a; });
 }
 __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, [](uint32_t a, uint32_t b) { return a | b; });
 }
 // Value of lane `l` (wave-uniform l) broadcast to every lane.
 __device__ __forceinline__ int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
@@ -95,51 +129,48 @@ __device__ __forceinline__ double readlane_d(double v, int l) {
   return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
-// Cross-lane moves within each row of 16 lanes (DPP, no LDS): XOR 1 and XOR 2
-// inside each quad, mirror within each half-row and within the row. Applied in
-// that order to a commutative reduction they leave the row's result in every
-// lane of the row.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
-
 // Sum / maximum over the 8 lanes of each half-row (lanes 0-7 hold the result
 // for lanes 0-7).
 __device__ __forceinline__ float lanes8_sum(float v) {
-  v += dpp_f<kDppQuadXor1>(v);
-  v += dpp_f<kDppQuadXor2>(v);
-  return v + dpp_f<kDppHalfMirror>(v);
+  v += dpp_move<kDppQuadXor1>(v);
+  v += dpp_move<kDppQuadXor2>(v);
+  return v + dpp_move<kDppHalfMirror>(v);
 }
 __device__ __forceinline__ float lanes8_max(float v) {
-  v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
-  v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
-  return fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_move<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_move<kDppQuadXor2>(v));
+  return fmaxf(v, dpp_move<kDppHalfMirror>(v));
 }
 // Wave64 sum / maximum without LDS: row reductions by DPP, then the four row
 // results read from lanes 0, 16, 32, 48 (the same order in every lane).
 __device__ __forceinline__ float wave_sum_dpp(float v) {
   v = lanes8_sum(v);
-  v += dpp_f<kDppMirror>(v);
+  v += dpp_move<kDppMirror>(v);
   return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
 __device__ __forceinline__ float wave_max_dpp(float v) {
   v = lanes8_max(v);
-  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  v = fmaxf(v, dpp_move<kDppMirror>(v));
   return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 
-// Inclusive prefix sum over lanes 0..63.
+// Inclusive prefix sum over lanes 0..63: the prefix within each row of 16 lanes by
+// DPP row shifts of 1, 2, 4 and 8 (lanes shifted in from outside the row add 0),
+// then the totals of the rows before, read from lanes 15, 31 and 47.
 template <typename T>
 __device__ __forceinline__ T wave_inclusive_scan(T v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    T w = __shfl_up(v, o, kWave);
-    if (lane >= o) v += w;
-  }
-  return v;
+  constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+  v = v + dpp_move<kRowShr1>(v);
+  v = v + dpp_move<kRowShr2>(v);
+  v = v + dpp_move<kRowShr4>(v);
+  v = v + dpp_move<kRowShr8>(v);
+  const T s0 = lane_read(v, 15), s1 = lane_read(v, 31), s2 = lane_read(v, 47);
+  const int row = int(threadIdx.x & (kWave - 1)) >> 4;
+  T off = T(0);
+  if (row >= 1) off = s0;
+  if (row >= 2) off = off + s1;
+  if (row >= 3) off = off + s2;
+  return row == 0 ? v : v + off;
 }
 
 // ---------------------------------------------------------------------------

@@ -48,7 +48,7 @@ constexpr double NEAR_TIE = 1e-6;
 constexpr int PER_TILE = VT * UNR;    // 16-byte chunks per tile
 
 constexpr int FLAG_TIE_ACCEPT = 1, FLAG_TIE_TOPP_P = 2, FLAG_TIE_TOPP_Q = 4,
-              FLAG_TIE_ICDF = 8, FLAG_Q_ZERO = 16, FLAG_RES_ZERO = 32, FLAG_OVERFLOW = 64;
+              FLAG_TIE_ICDF = 8, FLAG_Q_ZERO = 16, FLAG_RES_ZERO = 32;
 
 enum { ROW_OK = 0, ROW_OVERFLOW = 1 };
 
