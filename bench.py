@@ -57,8 +57,8 @@ ONLY = {"verify": "verify", "gemm_attn": "gated_lora_attn_4096x4096",
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-tv", action="store_true", help="skip the TV-loss leg")
     ap.add_argument("--no-sweep", action="store_true",
