@@ -123,6 +123,34 @@ def test_verify_many_ties():
     assert st["exact"] + st["near_tie"] == S
 
 
+def _one_wave_rows(n_planted, S=2, b=4, V=151936, seed=11):
+    """Rows whose largest values all sit in 16-byte chunks that the first wave of a
+    workgroup reads (chunk c = 8 elements, read by thread c % 256): that wave flags
+    far more chunks than the others."""
+    rng = np.random.default_rng(seed)
+    base = rng.normal(0.0, 1.0, (S, b, V))
+    j = np.arange(n_planted)
+    groups = -(-n_planted // 64)
+    step = (V // 8 // 256 - 1) // groups             # spread the groups of 64 along the row
+    chunks = 256 * (step * (j // 64)) + (j % 64)     # distinct chunks of lanes 0..63
+    cols = chunks * 8 + (j % 8)
+    assert cols.max() < V
+    base[:, :, cols] = 8.0 + rng.random((S, b, n_planted))
+    p = workloads.to_bf16_bits(base.astype(np.float32))
+    q = workloads.to_bf16_bits((base + rng.normal(0.0, 0.5, (S, b, V))).astype(np.float32))
+    return p, q
+
+
+@pytest.mark.parametrize("n_planted", [140, 400])
+def test_verify_one_wave_holds_the_top_values(n_planted):
+    """140: the first wave's own chunk list fills and the shared spill area takes the
+    rest; 400: the lists overflow and the slot takes the full-row path. Both match
+    the oracle."""
+    p, q = _one_wave_rows(n_planted)
+    st, _, _ = _run_full(p, q, SP)
+    assert st["exact"] + st["near_tie"] == p.shape[0]
+
+
 def test_verify_identical_rows_accept_everything():
     p, _ = workloads.verify_logits(dict(workloads.VERIFY_CONFIGS["qwen"], S=4, b=16), V=8192)
     st, gpu, _ = _run_full(p, p.copy(), SP)
