@@ -195,38 +195,10 @@ __device__ __forceinline__ void store_grad(E* row, int V, int c0, const float (&
   }
 }
 
-// Next-row prefetch (bf16 rows on the vector path): the workgroup's slices of
-// the next response row are copied into LDS by buffer loads that write LDS
-// directly, while the current row is computed and exchanged. Thread t's chunk u
-// of tensor x lands at pre[x][u][t].
-template <typename E, bool VEC> struct TvPrefetch { static constexpr bool on = false; };
-template <> struct TvPrefetch<uint16_t, true> { static constexpr bool on = false; };
-constexpr int PRE_CH = EPT / 8;          // 16-byte chunks per thread per tensor (bf16)
-
-__device__ __forceinline__ void prefetch_row(const uint16_t* trow, const uint16_t* srow, int V, int c0,
-                                             uint4* pre) {
-  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
-  const __amdgpu_buffer_rsrc_t rt = slice_rsrc(trow, V, c0, 2), rs = slice_rsrc(srow, V, c0, 2);
-#pragma unroll
-  for (int u = 0; u < PRE_CH; ++u) {
-    const uint32_t off = uint32_t((u * TT + int(threadIdx.x)) * 16);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (__attribute__((address_space(3))) void*)(pre + u * TT + wave * kWave),
-                                             16, off, 0, 0, kBufNonTemporal);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(pre + (PRE_CH + u) * TT + wave * kWave),
-                                             16, off, 0, 0, kBufNonTemporal);
-  }
-}
-
-// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void tv_wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // Team exchange without a counter: each member publishes its n partials as
 // tagged words (64-bit device-coherent stores, no wait), and every member polls
 // the team's words until all carry the current tag. Nothing older than the
-// record (gradient stores, LDS prefetches) has to retire first. Polls are bounded:
+// record (gradient stores) has to retire first. Polls are bounded:
 // a poll that runs out raises the abort flag, which every poller checks, so every
 // wait ends.
 __device__ __forceinline__ void publish(unsigned long long* rec, const float* v, int n, unsigned tag) {
@@ -297,64 +269,21 @@ __global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
   E* gbase = static_cast<E*>(a.grad);
   unsigned nbar = 0;
   bool ok = true;
-  constexpr bool PRE = TvPrefetch<E, VEC>::on;
-  __shared__ uint4 pre[PRE ? 2 * PRE_CH * TT : 1];
-  // Prefetch state: have_pre = the next masked row's slices are in flight to LDS;
-  // stores_after = this thread has issued a full row of gradient stores since.
-  // Vector memory operations complete in issue order, so the wait before reading
-  // the slices may leave those later stores in flight.
-  bool have_pre = false, stores_after = false;
-  auto prefetch_next = [&](int rn) {
-    if constexpr (PRE) {
-      if (rn < a.R && a.mask[rn] != 0) {
-        prefetch_row(reinterpret_cast<const uint16_t*>(tbase) + size_t(rn) * V,
-                     reinterpret_cast<const uint16_t*>(sbase) + size_t(rn) * V, V, c0, pre);
-        have_pre = true;
-        stores_after = false;
-      }
-    }
-  };
 
   for (int r = team; ok && r < a.R; r += pl.nteams) {
     E* grow = gbase ? gbase + size_t(r) * V : nullptr;
     if (a.mask[r] == 0) {
-      if (!have_pre) prefetch_next(r + pl.nteams);
       if (grow) {
         float z[EPT];
 #pragma unroll
         for (int j = 0; j < EPT; ++j) z[j] = 0.0f;
         store_grad<E, VEC>(grow, V, c0, z, z, 0.0f, 0.0f, true);
-        if (have_pre) stores_after = true;
       }
       if (member == 0 && tid == 0 && a.tv_rows) a.tv_rows[r] = 0.0f;
       continue;
     }
     float et[EPT], es[EPT];
-    if constexpr (PRE) {
-      if (!have_pre) {
-        prefetch_row(reinterpret_cast<const uint16_t*>(tbase) + size_t(r) * V,
-                     reinterpret_cast<const uint16_t*>(sbase) + size_t(r) * V, V, c0, pre);
-        stores_after = false;
-      }
-      if (stores_after) tv_wait_vmcnt<PRE_CH>();   // one row of gradient stores: PRE_CH per thread
-      else tv_wait_vmcnt<0>();
-      __syncthreads();
-#pragma unroll
-      for (int u = 0; u < PRE_CH; ++u) {
-        float v[8];
-        TvElem<uint16_t>::unpack(pre[u * TT + tid], v);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) et[u * 8 + j] = v[j];
-        TvElem<uint16_t>::unpack(pre[(PRE_CH + u) * TT + tid], v);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) es[u * 8 + j] = v[j];
-      }
-      __syncthreads();
-      have_pre = false;
-      prefetch_next(r + pl.nteams);
-    } else {
-      load_slices<E, VEC>(tbase + size_t(r) * V, sbase + size_t(r) * V, V, c0, et, es);
-    }
+    load_slices<E, VEC>(tbase + size_t(r) * V, sbase + size_t(r) * V, V, c0, et, es);
     if (c0 + CHUNK > V) {                       // last slice of the row: mask the tail
       constexpr int VN = TvElem<E>::VN;
       const int lim = V - c0 - tid * VN;        // element j is in the row iff (j/VN)*TT*VN + j%VN < lim
@@ -477,12 +406,10 @@ __global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     if (grow) {
       const float h = 0.5f * inv_tn, g0 = float(-gsum * double(inv_tn));
       store_grad<E, VEC>(grow, V, c0, et, es, h, g0, false);
-      if (have_pre) stores_after = true;
     }
     __syncthreads();                           // sh.rec reuse by the next row
   }
 
-  tv_wait_vmcnt<0>();                          // no LDS prefetch left in flight
   // ---- completion: the last workgroup reduces the loss in a fixed order ----
   if (tid == 0) {
     __builtin_amdgcn_s_waitcnt(0);
