@@ -135,8 +135,7 @@ int uno_verify_block(const void* p_logits, const void* q_logits, int dtype,
  * the draft half of a Psi-Spec step ("LoopUno", "How it works": the block is
  * drafted in one forward); its uniforms are independent of the verifier's.
  *   q_logits : [S, b, V] of `dtype`; draft_tokens : int32 [S, b] (out)
- *   flags    : int32 [S, b] (out, optional) UNO_FLAG_TIE_TOPP_Q / _TIE_ICDF /
- *              _OVERFLOW
+ *   flags    : int32 [S, b] (out, optional) UNO_FLAG_TIE_TOPP_Q / _TIE_ICDF
  * Same limits as uno_verify_block; needs no workspace.
  * ------------------------------------------------------------------------- */
 int uno_draft_sample(const void* q_logits, int dtype, const int64_t* seq_ids,
