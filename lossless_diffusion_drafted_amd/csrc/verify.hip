@@ -11,12 +11,18 @@
 // Design (one workgroup of 256 threads per slot):
 //  * The slot's p and q rows are streamed once from HBM, interleaved tile by tile
 //    (16-byte buffer loads, eight per thread per tile, one tile in flight while the
-//    other is scanned), into one LDS candidate list per row.
+//    other is scanned). Waves lower their issue priority as they progress, so the
+//    workgroups sharing a CU end their streams together.
 //  * A lower bound of each row's k-th largest logit comes from its first tile and
-//    is raised as the scan proceeds: each wave takes the ceil(k/4)-th largest of
-//    its 64 running lane maxima, so the minimum over the 4 waves has at least k
-//    row elements at or above it. For bf16 rows with a positive bound, eight
-//    elements are pre-checked with three packed 16-bit max instructions.
+//    is raised after each of the next tiles: each wave takes the ceil(k/4)-th
+//    largest of its 64 running lane maxima (a radix select, one ballot per key
+//    bit), so the minimum over the 4 waves has at least k row elements at or above
+//    it. For bf16 rows with a positive bound, eight elements are pre-checked with
+//    three packed 16-bit max instructions.
+//  * A 16-byte chunk that may reach the bound is stored whole in its wave's LDS
+//    list (ballot-ranked slots, no atomic), or in a spill area shared by the row's
+//    waves once that list is full. After the stream the chunks are expanded against
+//    the final bound into the row's candidate list.
 //  * After the stream, wave 0 selects and filters the p row while wave 1 does the
 //    q row, with no barriers: an MSB-first radix select over the candidates'
 //    order-preserving keys (only the bits where they differ) gives the exact
