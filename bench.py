@@ -82,23 +82,27 @@ def dev_tensor(a, device):
 
 
 class KernelTimer:
-    """Per-kernel HIP events on the current (launch) stream."""
+    """HIP events on the current (launch) stream around a run of n back-to-back calls
+    of one entry point; the average is the steady-state time per call (an event pair
+    around every single call would add the gap before each launch to it)."""
 
     def __init__(self):
         self.pairs = {}
 
-    def run(self, name, fn):
+    def run(self, name, fn, n=1):
         import torch
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
-        out = fn()
+        out = None
+        for _ in range(n):
+            out = fn()
         e.record()
-        self.pairs.setdefault(name, []).append((s, e))
+        self.pairs.setdefault(name, []).append((s, e, n))
         return out
 
     def avg_ms(self, name):
         p = self.pairs.get(name, [])
-        return sum(s.elapsed_time(e) for s, e in p) / max(1, len(p))
+        return sum(s.elapsed_time(e) for s, e, _ in p) / max(1, sum(n for _, _, n in p))
 
     def clear(self):
         self.pairs = {}
@@ -194,8 +198,7 @@ def run_only(args, uno, workloads, dev):
     for _ in range(args.warmup):
         fn()
     torch.cuda.synchronize()
-    for _ in range(args.steps):
-        timer.run(args.only, fn)
+    timer.run(args.only, fn, args.steps)
     torch.cuda.synchronize()
     print(json.dumps({"only": args.only, "calls": args.steps, "avg_us": timer.avg_ms(args.only) * 1000}))
 
@@ -317,11 +320,6 @@ def main():
             fn()
         verify_run()
 
-    def timed_step():
-        for name, (fn, _) in gemms.items():
-            timer.run(name, fn)
-        timer.run("verify", verify_run)
-
     # Headline: the step as a caller runs it, timed only at its boundaries (events
     # between the calls would each add a fence to the stream).
     for _ in range(args.warmup):
@@ -335,9 +333,11 @@ def main():
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
     positions = S * b
     value = positions / (ms_per_step / 1000.0)
-    # Per-call durations: the same steps again with HIP events around each call.
-    for _ in range(args.steps):
-        timed_step()
+    # Per-call durations: each entry point of the step run args.steps times back to
+    # back between one pair of HIP events.
+    for name, (fn, _) in gemms.items():
+        timer.run(name, fn, args.steps)
+    timer.run("verify", verify_run, args.steps)
     torch.cuda.synchronize()
 
     kernels = {}
@@ -424,8 +424,7 @@ def tv_benchmark(uno, workloads, dev, iters):
     torch.cuda.synchronize()
     n_resp = int(mask.sum().item())
     timer = KernelTimer()
-    for _ in range(iters):
-        timer.run("tv", lambda: uno.uno_tv_loss_fwd_bwd(t, s, mask, c["temperature"], want_rows=False))
+    timer.run("tv", lambda: uno.uno_tv_loss_fwd_bwd(t, s, mask, c["temperature"], want_rows=False), iters)
     torch.cuda.synchronize()
     ms = timer.avg_ms("tv")
     # teacher + student rows of response rows read once; gradient written for every row
@@ -456,9 +455,8 @@ def lora_bwd_benchmark(uno, workloads, dev, iters):
         f_wt()
         torch.cuda.synchronize()
         timer = KernelTimer()
-        for _ in range(iters):
-            timer.run("w", f_w)
-            timer.run("b", f_wt)
+        timer.run("w", f_w, iters)
+        timer.run("b", f_wt, iters)
         torch.cuda.synchronize()
         ms = timer.avg_ms("b")
         ms_w = timer.avg_ms("w")
@@ -496,8 +494,7 @@ def verify_sweep(uno, workloads, p_np, q_np, dev, iters):
             timer = KernelTimer()
             fn()
             torch.cuda.synchronize()
-            for _ in range(iters):
-                timer.run("v", fn)
+            timer.run("v", fn, iters)
             torch.cuda.synchronize()
             ms = timer.avg_ms("v")
             byts = verify_bytes(S, b, V)
