@@ -16,9 +16,7 @@
 //
 // Main loop: an NS-stage ring of LDS tiles filled by buffer loads that write LDS
 // directly (no staging registers), one counted vmcnt wait and one barrier per
-// reduction tile. In the pipelined form (wide tiles) each wave reads the
-// fragments of its next 16-wide step while the matrix pipe works on the current
-// one, in a fixed MFMA / LDS-read interleave. LDS rows are XOR-swizzled in 16-byte chunks so the 16-byte
+// reduction tile. LDS rows are XOR-swizzled in 16-byte chunks so the 16-byte
 // fragment reads of 16 consecutive rows hit distinct banks. Each wave owns a
 // (BM/WM) x (BN/WN) block of 32 x 32 v_mfma_f32_32x32x16_bf16 tiles. The output
 // is staged through LDS and written with 16-byte stores.
@@ -36,12 +34,9 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past any range: reads 0
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int NS_, bool PIPE_ = false>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int NS_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, NS = NS_;
-  // PIPE: the fragment reads of the next 16-wide step are issued under the
-  // MFMAs of the current one, and the tile barrier sits mid-tile.
-  static constexpr bool PIPE = PIPE_;
   static constexpr int NW = WM * WN;
   static constexpr int THREADS = NW * kWave;
   static constexpr int CPR = BK / 8;                 // 16-byte chunks per LDS row
@@ -64,12 +59,15 @@ struct Cfg {
   static constexpr int LDS_BYTES = (RING_BYTES + 1024) > OUT_BYTES ? (RING_BYTES + 1024) : OUT_BYTES;
   static_assert(BM * CPR % kWave == 0 && BN * CPR % kWave == 0, "tiles fill whole wave loads");
   static_assert((NS - 2) * L <= 63, "vmcnt holds at most 63 outstanding loads");
-  static_assert(!PIPE || (BK == 32 && NS >= 3), "pipelined loop: two 16-wide steps per tile");
   static_assert(CPR <= 16 && 16 % CPR == 0, "row chunking");
 };
 
-using CfgWide = Cfg<256, 192, 32, 4, 2, 5, true>;   // 8 waves of 64 x 96, pipelined
-using CfgSquare = Cfg<128, 128, 64, 2, 4, 2>; // 8 waves of 64 x 32
+// Both double-buffered with long reduction tiles: fewer barriers per MFMA did more
+// than deeper prefetch. Measured on 1024 rows: 5 stages of 32 with the fragment
+// reads pipelined under the MFMAs were 6% slower on 4096 -> 12288; 64-wide tiles
+// in 2 or 3 stages were 3-5% slower on 4096 -> 4096.
+using CfgWide = Cfg<256, 192, 64, 4, 2, 2>;    // 8 waves of 64 x 96
+using CfgSquare = Cfg<128, 128, 128, 2, 4, 2>; // 8 waves of 64 x 32
 
 struct Seg {
   const uint16_t* a;   // [M, k] row-major (X or T)
@@ -202,71 +200,6 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams p) {
     }
   };
 
-  if constexpr (C::PIPE) {
-    // Step j of tile t multiplies fragments read during step j - 1. The barrier
-    // of tile t sits before its second step: it publishes tile t + 1 (waited
-    // for with one tile still in flight behind it) and frees the stage of tile
-    // t - 1, whose fragments were all consumed in tile t - 1.
-    bf16x8_t fa0[C::MI], fb0[C::NJ], fa1[C::MI], fb1[C::NJ];
-    auto rd = [&](int st, int ks, bf16x8_t (&fa)[C::MI], bf16x8_t (&fb)[C::NJ]) {
-      const char* As = smem + st * C::STAGE_BYTES + arow;
-      const char* Bs = smem + st * C::STAGE_BYTES + C::A_BYTES + brow;
-      const int ch = ((2 * ks + fh) ^ fswz) * 16;
-#pragma unroll
-      for (int i = 0; i < C::MI; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(As + i * 32 * C::CPR * 16 + ch);
-#pragma unroll
-      for (int j = 0; j < C::NJ; ++j) fb[j] = *reinterpret_cast<const bf16x8_t*>(Bs + j * 32 * C::CPR * 16 + ch);
-    };
-    auto mm = [&](const bf16x8_t (&fa)[C::MI], const bf16x8_t (&fb)[C::NJ]) {
-#pragma unroll
-      for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-        for (int j = 0; j < C::NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    };
-#pragma unroll
-    for (int s = 0; s < C::NS - 1; ++s) issue(s, s);
-    wait_vmcnt<(C::NS - 2) * C::L>();
-    __builtin_amdgcn_s_barrier();
-    rd(0, 0, fa0, fb0);
-    int st = 0;
-#pragma unroll 1
-    for (int t = 0; t < ntiles; ++t) {
-      const int st1 = st + 1 == C::NS ? 0 : st + 1;
-      const int sti = st == 0 ? C::NS - 1 : st - 1;   // stage of t + NS - 1 (= t - 1)
-      // Each half is a fixed region (sched_barrier), in which the program
-      // order is MFMA, LDS read, MFMA, LDS read, ...: a read issues while the
-      // matrix pipe works through the MFMA before it, and the reads feed the
-      // next half.
-      rd(st, 1, fa1, fb1);
-      mm(fa0, fb0);
-#pragma unroll
-      for (int i = 0; i < C::MI + C::NJ; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, C::MI * C::NJ - C::MI - C::NJ, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<(C::NS - 3) * C::L>();
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      issue(t + C::NS - 1, sti);
-      rd(st1, 0, fa0, fb0);
-      mm(fa1, fb1);
-#pragma unroll
-      for (int i = 0; i < C::MI + C::NJ; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);   // LDS read
-      }
-#pragma unroll
-      for (int i = 0; i < C::MI * C::NJ - C::MI - C::NJ; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);   // global load into LDS
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      st = st1;
-    }
-  } else {
 #pragma unroll
   for (int s = 0; s < C::NS - 1; ++s) issue(s, s);
   // Unrolled by NS so every ring stage index is a constant.
@@ -283,7 +216,6 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams p) {
       issue(t + C::NS - 1, (s + C::NS - 1) % C::NS);
       compute(s);
     }
-  }
   }
   wait_vmcnt<0>();
   __syncthreads();
