@@ -296,3 +296,70 @@ def test_workspace_reuse_across_shapes():
         p, q = workloads.verify_logits(cfg, seed=S * 100 + b, V=4096)
         st, gpu, ref = _run_full(p, q, sp)
         assert st["exact"] + st["near_tie"] == S and st["exact"] >= S - 1, (S, b, st)
+
+
+def _chi2_ok(obs, expect_prob, n):
+    """Chi-square goodness of fit with bins of expected count < 5 pooled; tokens
+    outside the support must never appear."""
+    from scipy import stats
+    sup = expect_prob > 0
+    assert obs[~sup].sum() == 0
+    e = expect_prob[sup] * n
+    o = obs[sup].astype(np.float64)
+    small = e < 5
+    if small.any():
+        e = np.append(e[~small], e[small].sum())
+        o = np.append(o[~small], o[small].sum())
+    return stats.chisquare(o, e * o.sum() / e.sum()).pvalue
+
+
+def test_sampling_statistics_end_to_end():
+    """The HIP draft sampler and verifier over 10^5 blocks (the same filtered rows
+    in every block, independent Philox streams): drafts follow q~, every slot's
+    committed token follows p~ (lossless), the per-slot acceptance rate is
+    1 - TV(p~, q~) and the mean accept length 1 + sum_j prod_{i<=j} (1 - TV_i),
+    each within 4 standard deviations."""
+    import math
+    uno = _uno()
+    rng = np.random.default_rng(31)
+    S, b, V = 100000, 4, 64
+    T, k, top_p = 1.0, 20, 0.9
+    zp = workloads.to_bf16_bits(rng.normal(0, 1.5, (b, V)).astype(np.float32))
+    zq = workloads.to_bf16_bits(workloads.bf16_bits_to_f32(zp) + rng.normal(0, 0.8, (b, V)).astype(np.float32))
+    pf = [oracle.filter_logits(workloads.bf16_bits_to_f32(zp[i]), T, k, top_p) for i in range(b)]
+    qf = [oracle.filter_logits(workloads.bf16_bits_to_f32(zq[i]), T, k, top_p) for i in range(b)]
+
+    def dense(f):
+        d = np.zeros(V)
+        d[f.ids] = f.probs
+        return d
+
+    pd, qd = [dense(f) for f in pf], [dense(f) for f in qf]
+    tvs = [0.0] + [0.5 * np.abs(pd[i] - qd[i]).sum() for i in range(1, b)]
+    p = to_device(np.broadcast_to(zp, (S, b, V)).copy(), DEV)
+    q = to_device(np.broadcast_to(zq, (S, b, V)).copy(), DEV)
+    seq = to_device(np.arange(S, dtype=np.int64) + 7, DEV)
+    pos = to_device(np.full(S, 11, dtype=np.int64), DEV)
+    sp = dict(temperature=T, top_k=k, top_p=top_p, seed=2024)
+    d, _ = uno.uno_draft_sample(q, seq, pos, **sp)
+    r = uno.uno_verify_block(p, q, d, seq, pos, **sp)
+    torch.cuda.synchronize()
+    d = d.cpu().numpy()
+    r = {key: v.cpu().numpy() for key, v in r.items()}
+    for i in range(1, b):
+        assert _chi2_ok(np.bincount(d[:, i], minlength=V), qd[i], S) > 1e-4, ("draft", i)
+    L = r["accept_len"]
+    assert np.all((L >= 1) & (L <= b))
+    assert np.all(r["slot_accept"][:, 0] == 1)
+    for i in range(b):
+        reached = L >= i if i > 0 else np.ones(S, bool)
+        tok = r["out_tokens"][reached, i]
+        assert np.all(tok >= 0)
+        assert _chi2_ok(np.bincount(tok, minlength=V), pd[i], reached.sum()) > 1e-4, ("committed", i)
+    for i in range(1, b):
+        a = r["slot_accept"][:, i].mean()
+        sd = math.sqrt((1 - tvs[i]) * tvs[i] / S)
+        assert abs(a - (1 - tvs[i])) < 4 * sd + 1e-12, (i, a, 1 - tvs[i])
+    e = oracle.expected_accept_len(tvs)
+    Lf = L.astype(np.float64)
+    assert abs(Lf.mean() - e) < 4 * Lf.std() / math.sqrt(S), (Lf.mean(), e)
