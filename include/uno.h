@@ -73,7 +73,8 @@ typedef struct {
 #define UNO_FLAG_TIE_ICDF 8        /* the inverse-CDF draw lies within 1e-6*Z of a boundary */
 #define UNO_FLAG_Q_ZERO 16         /* draft token outside supp(q~): rejected                */
 #define UNO_FLAG_RES_ZERO 32       /* residual mass zero after a rejection: drew from p~    */
-#define UNO_FLAG_OVERFLOW 64       /* a row needed the full-row path (large tied support)   */
+#define UNO_FLAG_OVERFLOW 64       /* reserved: no call sets it (overflowing rows take the  */
+                                   /* full-row path, with the same results)                  */
 
 /* Human-readable name of a status code (static storage). */
 const char* uno_status_string(int status);
