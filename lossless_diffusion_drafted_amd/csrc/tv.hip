@@ -236,6 +236,18 @@ __device__ bool gather(const unsigned long long* team_rec, int G, int slot, int 
   return sh.ok != 0;
 }
 
+// Response-mask byte of row r, read through the scalar data cache (a wave-uniform
+// load counted apart from vector memory). A vector load here would wait for every
+// older vector memory operation, the previous row's gradient stores included,
+// before the row's own loads could issue. The aligned word holding the byte lies in
+// the same page as the byte.
+__device__ __forceinline__ bool row_in_mask(const uint8_t* mask, int r) {
+  typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
+  const uintptr_t p = reinterpret_cast<uintptr_t>(mask) + uintptr_t(r);
+  const uint32_t w = *reinterpret_cast<const_u32_ptr>(p & ~uintptr_t(3));
+  return ((w >> ((p & 3u) * 8u)) & 0xffu) != 0u;
+}
+
 template <typename E, bool VEC>
 __global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(4, 4))) void tv_kernel(TvArgs a, TvPlan pl) {
   __shared__ TvLds sh;
@@ -272,7 +284,7 @@ __global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 
   for (int r = team; ok && r < a.R; r += pl.nteams) {
     E* grow = gbase ? gbase + size_t(r) * V : nullptr;
-    if (a.mask[r] == 0) {
+    if (!row_in_mask(a.mask, r)) {
       if (grow) {
         float z[EPT];
 #pragma unroll
