@@ -100,6 +100,7 @@ struct Shared {
   Dist dist[2];
   unsigned red_u[VW][3];
   unsigned ures[2];
+  double u[2];           // the slot's u_acc, u_res (drawn by wave 2 during the selection)
 };
 
 struct FilterParams {
@@ -1424,6 +1425,7 @@ __global__ __launch_bounds__(VT) __attribute__((amdgpu_waves_per_eu(4))) void ve
   // path; otherwise the single-pass path runs and falls back to the full-row path
   // for a slot whose candidate list or top-k set overflows.
   bool use_full = fp.k_eff > KMAX_SINGLE_PASS && V > SEL_CAP;
+  bool drawn = false;                 // sh.u holds the slot's uniforms
   if (!use_full) {
     reset_row(Rp);
     reset_row(Rq);
@@ -1448,8 +1450,18 @@ __global__ __launch_bounds__(VT) __attribute__((amdgpu_waves_per_eu(4))) void ve
     }
     __syncthreads();
     if (cp <= WAVE_SEL_MAX && cq <= WAVE_SEL_MAX) {
+      drawn = true;
       if (wid == 0) wave_select(Rp, fp);
       if (wid == 1 && has_q) wave_select(Rq, fp);
+      if (wid == 2) {
+        // The slot's uniforms, drawn by an otherwise idle wave off the critical path.
+        const Philox4 ph = philox4x64_10(uint64_t(a.pos[s] + i), 0ull, 0ull, 0ull, a.sp.seed,
+                                         uint64_t(a.seq_ids[s]));
+        if ((tid & (kWave - 1)) == 0) {
+          sh.u[0] = word_to_uniform(ph.w[0]);
+          sh.u[1] = word_to_uniform(ph.w[1]);
+        }
+      }
     } else {
       if (Rp.status == ROW_OK) block_select(Rp, fp, sh);
       if (has_q && Rq.status == ROW_OK) block_select(Rq, fp, sh);
@@ -1461,10 +1473,16 @@ __global__ __launch_bounds__(VT) __attribute__((amdgpu_waves_per_eu(4))) void ve
     use_full = Rp.status != ROW_OK || (has_q && Rq.status != ROW_OK);
   }
 
-  const Philox4 ph = philox4x64_10(uint64_t(a.pos[s] + i), 0ull, 0ull, 0ull, a.sp.seed,
-                                   uint64_t(a.seq_ids[s]));
-  const double u_acc = word_to_uniform(ph.w[0]);
-  const double u_res = word_to_uniform(ph.w[1]);
+  double u_acc, u_res;
+  if (drawn) {
+    u_acc = sh.u[0];
+    u_res = sh.u[1];
+  } else {
+    const Philox4 ph = philox4x64_10(uint64_t(a.pos[s] + i), 0ull, 0ull, 0ull, a.sp.seed,
+                                     uint64_t(a.seq_ids[s]));
+    u_acc = word_to_uniform(ph.w[0]);
+    u_res = word_to_uniform(ph.w[1]);
+  }
   SlotResult res;
   if (use_full) {
     __shared__ FullLds fsh;
