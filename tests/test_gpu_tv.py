@@ -194,3 +194,25 @@ def test_tv_full_size_sampled_rows():
     g = grad[sample].float().cpu().numpy().astype(np.float64)
     for a in range(len(sample)):
         assert np.linalg.norm(g[a] - ref_grad[a]) <= 2e-2 * np.linalg.norm(ref_grad[a])
+
+
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_tv_mask_at_any_byte_offset(offset):
+    """The response mask is read a 4-byte word at a time through the scalar cache;
+    a mask that starts at any byte offset gives the same rows and gradient."""
+    uno = _uno()
+    R, V = 37, 5000
+    t, s = _inputs(R, V, "bf16", seed=11 + offset)
+    mask = (np.random.default_rng(offset).random(R) < 0.6).astype(np.uint8)
+    mask[0], mask[-1] = 1, 0
+    backing = np.zeros(R + 8, np.uint8)
+    backing[offset:offset + R] = mask
+    mdev = to_device(backing, DEV)[offset:offset + R]
+    assert mdev.data_ptr() % 4 == offset          # device allocations are at least 4-byte aligned
+    loss, rows, grad = uno.uno_tv_loss_fwd_bwd(to_device(t, DEV), to_device(s, DEV), mdev,
+                                               temperature=1.0, want_grad=True, want_rows=True)
+    torch.cuda.synchronize()
+    gpu = {"loss": float(loss.item()), "rows": rows.cpu().numpy().astype(np.float64),
+           "grad": grad.float().cpu().numpy().astype(np.float64)}
+    ref_loss, ref_rows, ref_grad = oracle.tv_loss_fwd_bwd(t, s, mask, 1.0, dtype="bf16")
+    _check(gpu, ref_loss, ref_rows, ref_grad, mask)
