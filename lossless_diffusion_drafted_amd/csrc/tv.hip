@@ -35,7 +35,10 @@
 namespace uno {
 namespace {
 
-constexpr int TT = 512;                 // threads per workgroup
+// One 1024-thread workgroup per CU; at V = 151936 a team is 4 workgroups. Measured
+// against 512-thread workgroups (two per CU, teams of 8): 5.24 against 5.76 ms on the
+// 32768 x 151936 self-distillation workload (fewer members per team exchange).
+constexpr int TT = 1024;                // threads per workgroup
 constexpr int TWAVES = TT / kWave;
 constexpr int EPT = 40;                 // elements of each row per thread
 constexpr int CHUNK = TT * EPT;         // elements of each row per workgroup
@@ -248,6 +251,16 @@ __device__ __forceinline__ bool row_in_mask(const uint8_t* mask, int r) {
   return ((w >> ((p & 3u) * 8u)) & 0xffu) != 0u;
 }
 
+// Sum / maximum over the 16 lanes of each row (lanes 0-15 hold the result).
+__device__ __forceinline__ float lanes16_sum(float v) {
+  v = lanes8_sum(v);
+  return v + dpp_move<kDppMirror>(v);
+}
+__device__ __forceinline__ float lanes16_max(float v) {
+  v = lanes8_max(v);
+  return fmaxf(v, dpp_move<kDppMirror>(v));
+}
+
 template <typename E, bool VEC>
 __global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(4, 4))) void tv_kernel(TvArgs a, TvPlan pl) {
   __shared__ TvLds sh;
@@ -330,8 +343,8 @@ __global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       zt += et[j];
       zs += es[j];
     }
-    // Wave partials (DPP reductions), then the workgroup partial over the eight
-    // waves in lanes 0-7 of wave 0, then the team.
+    // Wave partials (DPP reductions), then the workgroup partial over the sixteen
+    // waves in lanes 0-15 of wave 0, then the team.
     {
       const float wmt = wave_max_dpp(zt > 0.0f ? mt : -INFINITY);
       const float wms = wave_max_dpp(zs > 0.0f ? ms : -INFINITY);
@@ -344,10 +357,10 @@ __global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         const bool in = lane < TWAVES;
         const float m0 = in ? sh.wred[lane][0] : -INFINITY, z0 = in ? sh.wred[lane][1] : 0.0f;
         const float m1 = in ? sh.wred[lane][2] : -INFINITY, z1 = in ? sh.wred[lane][3] : 0.0f;
-        const float Mt = lanes8_max(z0 > 0.0f ? m0 : -INFINITY);
-        const float Ms = lanes8_max(z1 > 0.0f ? m1 : -INFINITY);
-        const float Zt = lanes8_sum(z0 > 0.0f ? z0 * __builtin_amdgcn_exp2f((m0 - Mt) * c) : 0.0f);
-        const float Zs = lanes8_sum(z1 > 0.0f ? z1 * __builtin_amdgcn_exp2f((m1 - Ms) * c) : 0.0f);
+        const float Mt = lanes16_max(z0 > 0.0f ? m0 : -INFINITY);
+        const float Ms = lanes16_max(z1 > 0.0f ? m1 : -INFINITY);
+        const float Zt = lanes16_sum(z0 > 0.0f ? z0 * __builtin_amdgcn_exp2f((m0 - Mt) * c) : 0.0f);
+        const float Zs = lanes16_sum(z1 > 0.0f ? z1 * __builtin_amdgcn_exp2f((m1 - Ms) * c) : 0.0f);
         if (lane == 0) {
           const float v[4] = {Mt, Zt, Ms, Zs};
           publish(my_rec, v, 4, epoch_tag | ((nbar + 1) & 0xffffu));
@@ -396,8 +409,8 @@ __global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
       __syncthreads();
       if (wid == 0) {
         const bool in = lane < TWAVES;
-        const float T = lanes8_sum(in ? sh.wred[lane][0] : 0.0f);
-        const float Gs = lanes8_sum(in ? sh.wred[lane][1] : 0.0f);
+        const float T = lanes16_sum(in ? sh.wred[lane][0] : 0.0f);
+        const float Gs = lanes16_sum(in ? sh.wred[lane][1] : 0.0f);
         if (lane == 0) {
           const float v[2] = {T, Gs};
           publish(my_rec + 4, v, 2, epoch_tag | ((nbar + 1) & 0xffffu));
