@@ -94,3 +94,24 @@ def test_tv_argument_validation(lib):
     assert _tv(lib, ws=64) == _lib.UNO_ERR_WORKSPACE
     assert _tv(lib, null_ws=True) == _lib.UNO_ERR_WORKSPACE
     assert lib.uno_tv_loss_workspace(32768, 151936) >= 32768 * 8
+
+
+def test_sampling_params_layout_matches_the_header(tmp_path):
+    """The ctypes mirror of uno_sampling_params has the size and field offsets that a
+    C compiler gives the struct declared in include/uno.h."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f for f, _ in _lib.SamplingParams._fields_]
+    body = " ".join(f'printf(" %zu", offsetof(uno_sampling_params, {f}));' for f in fields)
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "uno.h"\n'
+                   'int main(void) { printf("%zu", sizeof(uno_sampling_params)); '
+                   + body + ' printf("\\n"); return 0; }\n')
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [ctypes.sizeof(_lib.SamplingParams)] + [getattr(_lib.SamplingParams, f).offset for f in fields]
+    assert got == want, (got, want)

@@ -1,12 +1,13 @@
 """GPU parity of the HIP verifier and draft sampler against the CPU oracle.
 
 Token ids, accept lengths and resampled tokens must be bit-exact given the same
-Philox stream; a difference is tolerated only at a slot where either side flags
-a near-tie (|u - p~/q~| < 1e-6, a top-p boundary within 1e-6 of top_p, or an
-inverse-CDF draw within 1e-6*Z of a boundary), and such slots are counted.
-Draft tokens given to both sides come from the oracle's draft sampler; where a
-full-size workload is only sampled, the remaining sequences use the HIP draft
-sampler (their results are not compared).
+Philox stream; a difference is tolerated only from the first decisive slot (slot
+0, an accepted slot or the first rejected one) where either side flags a near-tie
+(|u - p~/q~| < 1e-6, a top-p boundary within 1e-6 of top_p, or an inverse-CDF draw
+within 1e-6*Z of a boundary); the tokens before it must still agree, and every
+other slot's raw accept decision must agree. Excused sequences are counted and
+printed, and each test bounds their number. Draft tokens given to both sides come
+from the oracle's draft sampler; the full-size workloads compare every sequence.
 """
 import numpy as np
 import pytest
@@ -14,7 +15,7 @@ import torch
 
 import oracle
 import workloads
-from helpers import compare_verify, dtype_name, to_device
+from helpers import assert_mostly_exact, compare_verify, dtype_name, to_device
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -84,7 +85,7 @@ def test_verify_qwen_distribution_reduced(V, S, b, seed):
     pos = rng.integers(0, 100000, S, dtype=np.int64)
     st, gpu, ref = _run_full(p, q, SP, seq, pos)
     print(V, S, b, st)
-    assert st["exact"] >= S - 1
+    assert_mostly_exact(st, S)
 
 
 @pytest.mark.parametrize("V,b,k,top_p,T", [
@@ -103,7 +104,7 @@ def test_verify_ragged_and_settings(V, b, k, top_p, T):
     sp = dict(temperature=T, top_k=k, top_p=top_p, seed=11)
     st, gpu, ref = _run_full(p, q, sp)
     print(V, b, k, top_p, T, st)
-    assert st["exact"] + st["near_tie"] == S and st["exact"] >= S - 1
+    assert_mostly_exact(st, S)
 
 
 def test_verify_fp32_unaligned_rows():
@@ -120,7 +121,8 @@ def test_verify_many_ties():
     p = workloads.to_bf16_bits(base.astype(np.float32))
     q = workloads.to_bf16_bits((base + np.round(rng.normal(0, 1, (S, b, V)) * 2) / 2).astype(np.float32))
     st, _, _ = _run_full(p, q, dict(SP, top_k=20))
-    assert st["exact"] + st["near_tie"] == S
+    print(st)
+    assert_mostly_exact(st, S)
 
 
 def _one_wave_rows(n_planted, S=2, b=4, V=151936, seed=11):
@@ -148,7 +150,8 @@ def test_verify_one_wave_holds_the_top_values(n_planted):
     the oracle."""
     p, q = _one_wave_rows(n_planted)
     st, _, _ = _run_full(p, q, SP)
-    assert st["exact"] + st["near_tie"] == p.shape[0]
+    print(n_planted, st)
+    assert_mostly_exact(st, p.shape[0])
 
 
 def test_verify_identical_rows_accept_everything():
@@ -168,47 +171,59 @@ def test_empty_batch_is_a_no_op():
 
 
 GREEDY = dict(SP, temperature=0.0)
+_FULL = {}
 
 
-@pytest.mark.parametrize("name,nsample,sp,b", [
-    ("qwen", 6, SP, None), ("looped", 6, SP, None), ("stress", 4, SP, None),
-    ("qwen", 6, GREEDY, None),          # greedy decoding at the metric's shape
-    ("qwen", 6, SP, 8),                 # block 8 at the metric's shape
+def _full_workload(name):
+    """The whole verify workload (generated once per module) and the oracle's drafts."""
+    if name not in _FULL:
+        _FULL.clear()                   # keep one workload's host arrays at a time
+        _FULL[name] = workloads.verify_logits(name)
+    return _FULL[name]
+
+
+@pytest.mark.parametrize("name,sp,b", [
+    ("qwen", SP, None), ("looped", SP, None), ("stress", SP, None),
+    ("qwen", GREEDY, None), ("looped", GREEDY, None), ("stress", GREEDY, None),
+    ("qwen", SP, 8),                    # block 8 at the metric's shape
+    ("qwen", GREEDY, 8),
 ])
-def test_verify_full_size_sampled(name, nsample, sp, b):
-    """Full-size workload in the benchmark's launch configuration; the oracle checks a
-    seeded sample of sequences."""
+def test_verify_full_size(name, sp, b):
+    """The full workload in the benchmark's launch configuration, every sequence
+    compared with the oracle: the HIP draft sampler against the oracle's drafts, then
+    the verifier on the oracle's drafts."""
     uno = _uno()
     c = workloads.VERIFY_CONFIGS[name]
-    S, V = c["S"], c["V"]
-    p, q = workloads.verify_logits(name)
+    S = c["S"]
+    p, q = _full_workload(name)
     if b is not None:                   # the first b slots of each block
         p, q = np.ascontiguousarray(p[:, :b]), np.ascontiguousarray(q[:, :b])
     b = p.shape[1]
     seq, pos = np.arange(S, dtype=np.int64), np.zeros(S, dtype=np.int64)
+    print(f"full-size verify {name} b={b} T={sp['temperature']}", flush=True)
     pd, qd = to_device(p, DEV), to_device(q, DEV)
-    dg, _ = uno.uno_draft_sample(qd, to_device(seq, DEV), to_device(pos, DEV), **sp)
+    seqd, posd = to_device(seq, DEV), to_device(pos, DEV)
+    dg, dflags = uno.uno_draft_sample(qd, seqd, posd, **sp)
     torch.cuda.synchronize()
-    d = dg.cpu().numpy()
-    pick = np.sort(np.random.default_rng(0).choice(S, nsample, replace=False))
-    dref, _ = oracle.draft_sample(q[pick], seq[pick], pos[pick], sp["temperature"], sp["top_k"],
-                                  sp["top_p"], sp["seed"], "bf16")
-    tie_free = np.array_equal(dref, d[pick])
-    d[pick] = dref                      # oracle drafts on the compared sequences
-    ref = oracle.verify_block(p[pick], q[pick], dref, seq[pick], pos[pick], sp["temperature"],
-                              sp["top_k"], sp["top_p"], sp["seed"], "bf16")
-    r = uno.uno_verify_block(pd, qd, to_device(d.astype(np.int32), DEV), to_device(seq, DEV),
-                             to_device(pos, DEV), **sp)
+    d_gpu, dflags = dg.cpu().numpy(), dflags.cpu().numpy()
+    dref, rflags = oracle.draft_sample(q, seq, pos, sp["temperature"], sp["top_k"], sp["top_p"], sp["seed"],
+                                       "bf16")
+    dtie = (dflags | rflags) & oracle.TIE_MASK
+    np.testing.assert_array_equal(d_gpu[dtie == 0], dref[dtie == 0])
+    ref = oracle.verify_block(p, q, dref, seq, pos, sp["temperature"], sp["top_k"], sp["top_p"], sp["seed"],
+                              "bf16")
+    r = uno.uno_verify_block(pd, qd, to_device(dref.astype(np.int32), DEV), seqd, posd, **sp)
     torch.cuda.synchronize()
     gpu = {k: v.cpu().numpy() for k, v in r.items()}
-    st = compare_verify(gpu, ref, b, seqs=pick)
+    st = compare_verify(gpu, ref, b)
     flags = gpu["diag"][..., 3].astype(np.int64)
-    print(name, st, "draft sampler exact on sample:", tie_free, "mean accept_len",
-          gpu["accept_len"].mean(), "overflow slots", int(np.sum(flags & 64 != 0)),
-          "near-tie slots", int(np.sum(flags & oracle.TIE_MASK != 0)))
-    assert st["exact"] >= nsample - 1
+    print(name, b, st, "draft near-tie slots", int(np.count_nonzero(dtie)), "mean accept_len",
+          gpu["accept_len"].mean(), "near-tie slots", int(np.sum(flags & oracle.TIE_MASK != 0)))
+    assert np.count_nonzero(dtie) <= 2
+    assert_mostly_exact(st, S, max_excused=2)
     assert not np.any(flags & 64)
     assert np.all((gpu["accept_len"] >= 1) & (gpu["accept_len"] <= b))
+    del pd, qd
 
 
 def test_repeat_runs_are_identical():
@@ -243,7 +258,7 @@ def test_verify_full_row_path(V, b, k, top_p, T, dtype):
     sp = dict(temperature=T, top_k=k, top_p=top_p, seed=5)
     st, gpu, ref = _run_full(p, q, sp)
     print(V, b, k, top_p, T, dtype, st)
-    assert st["exact"] + st["near_tie"] == S and st["exact"] >= S - 1
+    assert_mostly_exact(st, S)
 
 
 @pytest.mark.parametrize("V,k,top_p", [(40000, 0, 0.95), (20000, 500, 1.0)])
@@ -272,7 +287,8 @@ def test_massive_ties_take_the_full_row_path():
     z[1, :, 17] = 1.0                                     # one sequence with a unique maximum
     st, gpu, ref = _run_full(z, z.copy(), SP)
     assert not np.any(gpu["diag"][..., 3].astype(np.int64) & 64)
-    assert st["exact"] + st["near_tie"] == S
+    print(st)
+    assert_mostly_exact(st, S)
 
 
 def test_greedy_ties_take_the_lowest_id():
@@ -295,7 +311,8 @@ def test_workspace_reuse_across_shapes():
         cfg = dict(workloads.VERIFY_CONFIGS["qwen"], S=S, b=b)
         p, q = workloads.verify_logits(cfg, seed=S * 100 + b, V=4096)
         st, gpu, ref = _run_full(p, q, sp)
-        assert st["exact"] + st["near_tie"] == S and st["exact"] >= S - 1, (S, b, st)
+        print(S, b, st)
+        assert_mostly_exact(st, S)
 
 
 def _chi2_ok(obs, expect_prob, n):

@@ -31,6 +31,9 @@ Every logit row is generated from its own PCG64 stream keyed by (seed, workload,
 sequence, slot), so any subset of rows can be regenerated on its own.
 """
 
+import concurrent.futures
+import os
+
 import numpy as np
 
 VERIFY_CONFIGS = {
@@ -96,10 +99,12 @@ def logit_row_pair(cfg, s, i, seed=0, V=None):
     return base, draft.astype(np.float32)
 
 
-def verify_logits(cfg, seed=0, seqs=None, V=None):
+def verify_logits(cfg, seed=0, seqs=None, V=None, threads=None):
     """Base and draft logits [S', b, V] for the listed sequences (default: all).
 
-    bf16 workloads return uint16 bit patterns, fp32 workloads float32 values.
+    bf16 workloads return uint16 bit patterns, fp32 workloads float32 values. Rows
+    are drawn on a thread pool (numpy's generators release the GIL while they fill
+    a row); each row has its own stream, so the result does not depend on `threads`.
     """
     c = VERIFY_CONFIGS[cfg] if isinstance(cfg, str) else cfg
     V = c["V"] if V is None else V
@@ -108,7 +113,9 @@ def verify_logits(cfg, seed=0, seqs=None, V=None):
     out_t = np.uint16 if c["dtype"] == "bf16" else np.float32
     p = np.empty((n, c["b"], V), dtype=out_t)
     q = np.empty((n, c["b"], V), dtype=out_t)
-    for a, s in enumerate(seqs):
+
+    def fill(job):
+        a, s = job
         for i in range(c["b"]):
             base, draft = logit_row_pair(cfg, s, i, seed, V)
             if c["dtype"] == "bf16":
@@ -117,6 +124,15 @@ def verify_logits(cfg, seed=0, seqs=None, V=None):
             else:
                 p[a, i] = base
                 q[a, i] = draft
+
+    jobs = list(enumerate(seqs))
+    nthreads = min(16, os.cpu_count() or 1) if threads is None else max(1, int(threads))
+    if nthreads == 1 or n * c["b"] * V < (1 << 22):
+        for job in jobs:
+            fill(job)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(fill, jobs))
     return p, q
 
 
