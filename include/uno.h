@@ -18,7 +18,8 @@
  * Conventions shared by every call:
  *  - Every tensor pointer is DEVICE memory owned by the caller. The library never
  *    frees caller memory and keeps no per-call state between calls other than the
- *    caller-provided workspace.
+ *    caller-provided workspace (and, for uno_verify_block_noalloc only, one static
+ *    scratch array per GPU inside the library).
  *  - All work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
  *    default stream) and runs asynchronously; results are valid after the caller
  *    synchronises the stream.
@@ -129,6 +130,29 @@ int uno_verify_block(const void* p_logits, const void* q_logits, int dtype,
                      uno_sampling_params sp, int32_t* out_tokens, int32_t* accept_len,
                      int32_t* resampled, uint8_t* slot_accept, float* diag,
                      void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * uno_verify_block for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, results and kernels as uno_verify_block, without the workspace: the
+ * per-sequence tickets and slot records live in a static device array inside the
+ * library (1310720 bytes per GPU, held until the process ends). The call makes no
+ * hipMalloc, hipFree or other allocating call; the first call on a device looks
+ * up that GPU's copy of the array and clears it with a fill kernel on `stream`.
+ * Every verify kernel leaves the part it used zero again.
+ * Limit: the tickets and records, round_up(4 S, 256) + 8 S b bytes (what
+ * uno_verify_block_workspace returns), must fit the 1310720-byte array: any call
+ * with S <= 65536 sequences and S * b <= 131072 slots does. Larger calls return
+ * UNO_ERR_UNSUPPORTED (nothing launched) and must use uno_verify_block.
+ * All calls on one GPU share its array: calls that overlap in time on that GPU
+ * (on different streams, or from different threads) race and give wrong results.
+ * Serialise them, or give each its own workspace through uno_verify_block.
+ * ------------------------------------------------------------------------- */
+int uno_verify_block_noalloc(const void* p_logits, const void* q_logits, int dtype,
+                             const int32_t* draft_tokens, const int64_t* seq_ids,
+                             const int64_t* pos_offsets, int S, int b, int V,
+                             uno_sampling_params sp, int32_t* out_tokens, int32_t* accept_len,
+                             int32_t* resampled, uint8_t* slot_accept, float* diag, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Draft sampler: d[s,i] ~ filter(q_logits[s,i]) for every slot, by inverse CDF

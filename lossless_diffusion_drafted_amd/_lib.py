@@ -31,7 +31,7 @@ FLAG_TIE_MASK = FLAG_TIE_ACCEPT | FLAG_TIE_TOPP_P | FLAG_TIE_TOPP_Q | FLAG_TIE_I
 
 EXPORTS = [
     "uno_status_string", "uno_last_error", "uno_abi_version", "uno_workspace_init",
-    "uno_verify_block_workspace", "uno_verify_block", "uno_draft_sample",
+    "uno_verify_block_workspace", "uno_verify_block", "uno_verify_block_noalloc", "uno_draft_sample",
     "uno_tv_loss_workspace", "uno_tv_loss_fwd_bwd",
     "uno_gated_lora_linear_workspace", "uno_gated_lora_linear",
     "uno_gated_lora_linear_bwd_workspace", "uno_gated_lora_linear_bwd",
@@ -77,6 +77,8 @@ def load():
             "uno_verify_block_workspace": (_SZ, [_I, _I, _I]),
             "uno_verify_block": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, SamplingParams,
                                       _P, _P, _P, _P, _P, _P, _SZ, _P]),
+            "uno_verify_block_noalloc": (_I, [_P, _P, _I, _P, _P, _P, _I, _I, _I, SamplingParams,
+                                              _P, _P, _P, _P, _P, _P]),
             "uno_draft_sample": (_I, [_P, _I, _P, _P, _I, _I, _I, SamplingParams, _P, _P, _P]),
             "uno_tv_loss_workspace": (_SZ, [_I, _I]),
             "uno_tv_loss_fwd_bwd": (_I, [_P, _P, _I, _P, _I, _I, ctypes.c_float, _P, _P, _P,

@@ -86,6 +86,47 @@ size_t uno_verify_block_workspace(int S, int b, int V) {
   return uno::verify_workspace_bytes(S, b);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Argument checks and marshalling shared by both verify entry points.
+int verify_prepare(const char* fn, const void* p_logits, const void* q_logits, int dtype,
+                   const int32_t* draft_tokens, const int64_t* seq_ids, const int64_t* pos_offsets,
+                   int S, int b, int V, const uno_sampling_params& sp, int32_t* out_tokens,
+                   int32_t* accept_len, int32_t* resampled, uint8_t* slot_accept, float* diag,
+                   uno::VerifyArgs* a) {
+  int st = check_sampling(sp, S, b, V, fn);
+  if (st != UNO_OK) return st;
+  if (dtype != UNO_DTYPE_F32 && dtype != UNO_DTYPE_BF16)
+    return fail(UNO_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+  if (S == 0) return UNO_OK;
+  if (!p_logits || !q_logits || !draft_tokens || !seq_ids || !pos_offsets || !out_tokens ||
+      !accept_len || !resampled)
+    return fail(UNO_ERR_INVALID_ARG, "%s: a required pointer is null", fn);
+  a->p = p_logits;
+  a->q = q_logits;
+  a->bf16 = dtype == UNO_DTYPE_BF16;
+  a->draft = draft_tokens;
+  a->seq_ids = seq_ids;
+  a->pos = pos_offsets;
+  a->S = S;
+  a->b = b;
+  a->V = V;
+  a->sp = to_args(sp);
+  a->out_tokens = out_tokens;
+  a->accept_len = accept_len;
+  a->resampled = resampled;
+  a->slot_accept = slot_accept;
+  a->diag = diag;
+  a->ws = nullptr;
+  return UNO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int uno_verify_block(const void* p_logits, const void* q_logits, int dtype,
                      const int32_t* draft_tokens, const int64_t* seq_ids,
                      const int64_t* pos_offsets, int S, int b, int V,
@@ -93,35 +134,37 @@ int uno_verify_block(const void* p_logits, const void* q_logits, int dtype,
                      int32_t* resampled, uint8_t* slot_accept, float* diag,
                      void* workspace, size_t ws_bytes, void* stream) {
   const char* fn = "uno_verify_block";
-  int st = check_sampling(sp, S, b, V, fn);
-  if (st != UNO_OK) return st;
-  if (dtype != UNO_DTYPE_F32 && dtype != UNO_DTYPE_BF16)
-    return fail(UNO_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
-  if (S == 0) return ok();
-  if (!p_logits || !q_logits || !draft_tokens || !seq_ids || !pos_offsets || !out_tokens ||
-      !accept_len || !resampled)
-    return fail(UNO_ERR_INVALID_ARG, "%s: a required pointer is null", fn);
+  uno::VerifyArgs a;
+  int st = verify_prepare(fn, p_logits, q_logits, dtype, draft_tokens, seq_ids, pos_offsets, S, b, V, sp,
+                          out_tokens, accept_len, resampled, slot_accept, diag, &a);
+  if (st != UNO_OK || S == 0) return st == UNO_OK ? ok() : st;
   const size_t need = uno_verify_block_workspace(S, b, V);
   if (!workspace || ws_bytes < need)
     return fail(UNO_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, need);
-  uno::VerifyArgs a;
-  a.p = p_logits;
-  a.q = q_logits;
-  a.bf16 = dtype == UNO_DTYPE_BF16;
-  a.draft = draft_tokens;
-  a.seq_ids = seq_ids;
-  a.pos = pos_offsets;
-  a.S = S;
-  a.b = b;
-  a.V = V;
-  a.sp = to_args(sp);
-  a.out_tokens = out_tokens;
-  a.accept_len = accept_len;
-  a.resampled = resampled;
-  a.slot_accept = slot_accept;
-  a.diag = diag;
   a.ws = workspace;
   return hip_status(uno::launch_verify(a, static_cast<hipStream_t>(stream)), "uno_verify_block launch");
+}
+
+int uno_verify_block_noalloc(const void* p_logits, const void* q_logits, int dtype,
+                             const int32_t* draft_tokens, const int64_t* seq_ids,
+                             const int64_t* pos_offsets, int S, int b, int V,
+                             uno_sampling_params sp, int32_t* out_tokens, int32_t* accept_len,
+                             int32_t* resampled, uint8_t* slot_accept, float* diag, void* stream) {
+  const char* fn = "uno_verify_block_noalloc";
+  uno::VerifyArgs a;
+  int st = verify_prepare(fn, p_logits, q_logits, dtype, draft_tokens, seq_ids, pos_offsets, S, b, V, sp,
+                          out_tokens, accept_len, resampled, slot_accept, diag, &a);
+  if (st != UNO_OK || S == 0) return st == UNO_OK ? ok() : st;
+  const size_t need = uno::verify_workspace_bytes(S, b);
+  if (need > uno::verify_scratch_bytes())
+    return fail(UNO_ERR_UNSUPPORTED,
+                "%s: S = %d sequences of b = %d slots need %zu bytes of scratch and the library's "
+                "array holds %zu (S <= 65536 with S * b <= 131072 always fits); call "
+                "uno_verify_block with a workspace instead", fn, S, b, need, uno::verify_scratch_bytes());
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = uno::verify_scratch(&a.ws, hs);
+  if (e != hipSuccess) return hip_status(e, "uno_verify_block_noalloc scratch set-up");
+  return hip_status(uno::launch_verify(a, hs), "uno_verify_block_noalloc launch");
 }
 
 int uno_draft_sample(const void* q_logits, int dtype, const int64_t* seq_ids,

@@ -69,6 +69,10 @@ struct GemmArgs {
 
 size_t verify_workspace_bytes(int S, int b);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
+// The verifier's library-owned scratch (a static device array): its size, and its
+// device address on the current device, cleared on `stream` at the first request.
+size_t verify_scratch_bytes();
+hipError_t verify_scratch(void** out, hipStream_t stream);
 hipError_t launch_draft(const DraftArgs& a, hipStream_t stream);
 size_t tv_workspace_bytes(int R);
 int tv_max_vocab(bool bf16);          // largest V one row team covers on this device

@@ -34,6 +34,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -1666,6 +1668,44 @@ hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t stream) {
     hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, stream, static_cast<uint32_t*>(ptr), n);
   }
   return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------------------
+// Library-owned scratch of the verifier, for callers that cannot allocate
+// (uno_verify_block_noalloc). It holds the per-sequence tickets and slot records
+// that a caller workspace holds otherwise, laid out the same way. Each GPU has its
+// own copy of the array; host code reaches it only through the device address
+// hipGetSymbolAddress returns for the current device, never through its name.
+namespace {
+constexpr size_t kVerifyScratchBytes = 1310720;   // 256 KiB of tickets + 1 MiB of slot records
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kVerifyScratchBytes];
+}  // namespace
+
+size_t verify_scratch_bytes() { return kVerifyScratchBytes; }
+
+hipError_t verify_scratch(void** out, hipStream_t stream) {
+  static std::mutex mu;
+  static void* ptrs[kScratchDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    // Device globals start zeroed; clear the array once more on the first caller's
+    // stream so that its first call is ordered after a clear it can see. Every
+    // verify call leaves the part it used zero again.
+    e = launch_zero(p, kVerifyScratchBytes, stream);
+    if (e != hipSuccess) return e;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
 }
 
 }  // namespace uno

@@ -15,16 +15,7 @@ def sampling_params(temperature=1.0, top_k=50, top_p=0.95, seed=0):
     return SamplingParams(float(temperature), float(top_p), int(top_k), int(seed) & (2**64 - 1))
 
 
-def uno_verify_block(p_logits, q_logits, draft_tokens, seq_ids, pos_offsets,
-                     temperature=1.0, top_k=50, top_p=0.95, seed=0,
-                     want_slot_accept=True, want_diag=True, out=None):
-    """Lossless verification of a [S, b, V] block (see uno_verify_block in uno.h).
-
-    Returns a dict of device tensors: out_tokens [S,b] int32, accept_len [S] int32,
-    resampled [S] int32, and optionally slot_accept [S,b] uint8, diag [S,b,4] f32.
-    `out` may pass preallocated tensors under the same keys.
-    """
-    lib = load()
+def _verify_outputs(p_logits, q_logits, draft_tokens, seq_ids, pos_offsets, want_slot_accept, want_diag, out):
     if p_logits.dim() != 3:
         raise ValueError("p_logits must be [S, b, V]")
     S, b, V = p_logits.shape
@@ -45,6 +36,21 @@ def uno_verify_block(p_logits, q_logits, draft_tokens, seq_ids, pos_offsets,
         o["slot_accept"] = torch.empty((S, b), dtype=torch.uint8, device=dev)
     if want_diag and "diag" not in o:
         o["diag"] = torch.empty((S, b, 4), dtype=torch.float32, device=dev)
+    return S, b, V, dev, o
+
+
+def uno_verify_block(p_logits, q_logits, draft_tokens, seq_ids, pos_offsets,
+                     temperature=1.0, top_k=50, top_p=0.95, seed=0,
+                     want_slot_accept=True, want_diag=True, out=None):
+    """Lossless verification of a [S, b, V] block (see uno_verify_block in uno.h).
+
+    Returns a dict of device tensors: out_tokens [S,b] int32, accept_len [S] int32,
+    resampled [S] int32, and optionally slot_accept [S,b] uint8, diag [S,b,4] f32.
+    `out` may pass preallocated tensors under the same keys.
+    """
+    lib = load()
+    S, b, V, dev, o = _verify_outputs(p_logits, q_logits, draft_tokens, seq_ids, pos_offsets,
+                                      want_slot_accept, want_diag, out)
     stream = stream_handle(dev)
     nws = lib.uno_verify_block_workspace(S, b, V)
     ws = WORKSPACES.get(dev, stream, "verify", nws)
@@ -55,6 +61,24 @@ def uno_verify_block(p_logits, q_logits, draft_tokens, seq_ids, pos_offsets,
                               ptr(o.get("slot_accept")), ptr(o.get("diag")),
                               ptr(ws), ws.numel(), stream)
     check(st, "uno_verify_block")
+    return o
+
+
+def uno_verify_block_noalloc(p_logits, q_logits, draft_tokens, seq_ids, pos_offsets,
+                             temperature=1.0, top_k=50, top_p=0.95, seed=0,
+                             want_slot_accept=True, want_diag=True, out=None):
+    """uno_verify_block without a workspace: the library's own device scratch holds the
+    tickets and slot records (see uno_verify_block_noalloc in uno.h). With every output
+    passed in `out`, this call allocates nothing on the device."""
+    lib = load()
+    S, b, V, dev, o = _verify_outputs(p_logits, q_logits, draft_tokens, seq_ids, pos_offsets,
+                                      want_slot_accept, want_diag, out)
+    sp = sampling_params(temperature, top_k, top_p, seed)
+    st = lib.uno_verify_block_noalloc(ptr(p_logits), ptr(q_logits), _lib.dtype_code(p_logits),
+                                      ptr(draft_tokens), ptr(seq_ids), ptr(pos_offsets), S, b, V, sp,
+                                      ptr(o["out_tokens"]), ptr(o["accept_len"]), ptr(o["resampled"]),
+                                      ptr(o.get("slot_accept")), ptr(o.get("diag")), stream_handle(dev))
+    check(st, "uno_verify_block_noalloc")
     return o
 
 

@@ -115,3 +115,17 @@ def test_sampling_params_layout_matches_the_header(tmp_path):
     got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     want = [ctypes.sizeof(_lib.SamplingParams)] + [getattr(_lib.SamplingParams, f).offset for f in fields]
     assert got == want, (got, want)
+
+
+def test_noalloc_verify_rejects_sizes_beyond_its_scratch(lib):
+    """Checked on the host before any HIP call: 4096 x 64 slots need more than the
+    library's 1310720-byte verify scratch."""
+    sp = _lib.SamplingParams(1.0, 0.95, 50, 0)
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    st = lib.uno_verify_block_noalloc(fake, fake, 1, fake, fake, fake, 4096, 64, 1024, sp,
+                                      fake, fake, fake, None, None, None)
+    assert st == _lib.UNO_ERR_UNSUPPORTED
+    assert b"scratch" in lib.uno_last_error()
+    st = lib.uno_verify_block_noalloc(fake, fake, 1, fake, fake, fake, 4, 0, 1024, sp,
+                                      fake, fake, fake, None, None, None)
+    assert st == _lib.UNO_ERR_INVALID_ARG
