@@ -342,6 +342,222 @@ __global__ __launch_bounds__(LD_WAVES * 64) void lora_down_kernel(const uint16_t
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small-M path. With M <= 64 rows (a decode step's block rows) the tiled kernel
+// leaves most CUs idle, and the product is bound by reading W once from HBM.
+// Each workgroup owns 32 output columns and one of KS slices of the reduction;
+// its four waves split the slice into contiguous runs of 128-wide groups. A wave
+// multiplies its 32 W rows (two 16-column blocks) against every X row with
+// v_mfma_f32_16x16x32_bf16, M padded to 16-row blocks.
+//   The reduction index of each MFMA is permuted the same way on both operands:
+// in a 128-wide group, lane group g (lanes 16 g .. 16 g + 15) covers k = 32 g ..
+// 32 g + 31 and feeds 8 of them to each of the group's four MFMAs. Each lane's W
+// and X loads are therefore 64 contiguous bytes, and a W row is read in 256-byte
+// runs. The delta segment [T | B] (r more reduction steps, T already scaled and
+// gated) is taken 32 wide by the tile's last wave.
+//   The four wave partials meet in LDS in wave order. With KS > 1 each slice
+// stores its fp32 tile with device-coherent stores and takes a ticket; the last
+// slice of a column tile to finish adds the KS tiles in slice order (so the sum
+// order is fixed), writes bf16 and resets the ticket.
+struct SkinnyParams {
+  const uint16_t* x;      // [M, K]
+  const uint16_t* w;      // [N, K]
+  const uint16_t* t;      // [M, r] delta rows (scaled and gated), or null when r == 0
+  const uint16_t* b;      // [N, r]
+  int M, N, K, r, KS;
+  float scale;            // epilogue: y = mask[m] ? scale * acc : 0 (mask may be null)
+  const uint8_t* mask;
+  uint16_t* y;            // [M, N] bf16
+  float* part;            // [KS, M, N] fp32 slice tiles (KS > 1)
+  unsigned* ticket;       // [ceil(N / 32)], zero on entry and on exit
+};
+
+constexpr int SK_COLS = 32;        // output columns per workgroup
+constexpr int SK_GROUP = 128;      // reduction elements per group
+
+template <int MB>
+__global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  constexpr int NB = SK_COLS / 16;
+  constexpr int ROWS = MB * 16;
+  __shared__ float red[4][ROWS][SK_COLS + 1];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = blockIdx.x, ks = blockIdx.y;
+  const int n0 = tile * SK_COLS;
+  const int G = p.K / SK_GROUP;
+  const int nw = p.KS * 4, wi = ks * 4 + wave;
+  const int g0 = int((long long)G * wi / nw), g1 = int((long long)G * (wi + 1) / nw);
+  const int fr = lane & 15, fg = lane >> 4;
+
+  const __amdgpu_buffer_rsrc_t rx = make_row_rsrc(p.x, uint32_t(size_t(p.M) * p.K * 2));
+  const __amdgpu_buffer_rsrc_t rw = make_row_rsrc(p.w, uint32_t(size_t(p.N) * p.K * 2));
+  uint32_t xo[MB], wo[NB];
+  bool xin[MB], win[NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int m = i * 16 + fr;
+    xin[i] = m < p.M;
+    xo[i] = uint32_t((size_t(m) * p.K + fg * 32) * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int n = n0 + j * 16 + fr;
+    win[j] = n < p.N;
+    wo[j] = uint32_t((size_t(n) * p.K + fg * 32) * 2);
+  }
+
+  f32x4_t acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  u32x4_t xa[MB][4], wa[NB][4], xb[MB][4], wb[NB][4];
+  auto load = [&](int g, u32x4_t (&xv)[MB][4], u32x4_t (&wv)[NB][4]) {
+    const uint32_t kb = uint32_t(g) * SK_GROUP * 2;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        wv[j][c] = __builtin_amdgcn_raw_buffer_load_b128(rw, win[j] ? wo[j] + kb + c * 16 : kOutOfRange, 0u,
+                                                         kBufNonTemporal);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        xv[i][c] = __builtin_amdgcn_raw_buffer_load_b128(rx, xin[i] ? xo[i] + kb + c * 16 : kOutOfRange, 0u, 0);
+  };
+  auto mma = [&](const u32x4_t (&xv)[MB][4], const u32x4_t (&wv)[NB][4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xv[i][c]),
+                                                              __builtin_bit_cast(bf16x8_t, wv[j][c]),
+                                                              acc[i][j], 0, 0, 0);
+  };
+  // Two register sets, so every index is a constant: the next group's loads are in
+  // flight while the current group is multiplied.
+  if (g0 < g1) load(g0, xa, wa);
+  for (int g = g0; g < g1; g += 2) {
+    if (g + 1 < g1) load(g + 1, xb, wb);
+    mma(xa, wa);
+    if (g + 1 < g1) {
+      if (g + 2 < g1) load(g + 2, xa, wa);
+      mma(xb, wb);
+    }
+  }
+
+  // Delta segment: r more reduction steps, 32 wide, on the tile's last wave.
+  if (p.r > 0 && wi == nw - 1) {
+    const __amdgpu_buffer_rsrc_t rt = make_row_rsrc(p.t, uint32_t(size_t(p.M) * p.r * 2));
+    const __amdgpu_buffer_rsrc_t rb = make_row_rsrc(p.b, uint32_t(size_t(p.N) * p.r * 2));
+    for (int s0 = 0; s0 < p.r; s0 += 32) {
+      u32x4_t tv[MB], bv[NB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int m = i * 16 + fr;
+        tv[i] = __builtin_amdgcn_raw_buffer_load_b128(
+            rt, m < p.M ? uint32_t((size_t(m) * p.r + s0 + fg * 8) * 2) : kOutOfRange, 0u, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int n = n0 + j * 16 + fr;
+        bv[j] = __builtin_amdgcn_raw_buffer_load_b128(
+            rb, n < p.N ? uint32_t((size_t(n) * p.r + s0 + fg * 8) * 2) : kOutOfRange, 0u, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tv[i]),
+                                                              __builtin_bit_cast(bf16x8_t, bv[j]),
+                                                              acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // Accumulator v of lane l of a 16 x 16 block is row 4 (l / 16) + v, column l % 16.
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wave][i * 16 + 4 * fg + v][j * 16 + fr] = acc[i][j][v];
+  __syncthreads();
+
+  auto epilogue = [&](int m, float s) -> uint16_t {
+    const float y = (p.mask && p.mask[m] == 0) ? 0.0f : p.scale * s;
+    return __builtin_bit_cast(uint16_t, (__bf16)y);
+  };
+  const int rows = p.M < ROWS ? p.M : ROWS;
+  if (p.KS == 1) {
+    for (int e = tid; e < rows * SK_COLS; e += 256) {
+      const int m = e / SK_COLS, c = e % SK_COLS, n = n0 + c;
+      if (n >= p.N) continue;
+      const float s = red[0][m][c] + red[1][m][c] + red[2][m][c] + red[3][m][c];
+      p.y[size_t(m) * p.N + n] = epilogue(m, s);
+    }
+    return;
+  }
+  float* part = p.part + size_t(ks) * p.M * p.N;
+  for (int e = tid; e < rows * SK_COLS; e += 256) {
+    const int m = e / SK_COLS, c = e % SK_COLS, n = n0 + c;
+    if (n >= p.N) continue;
+    const float s = red[0][m][c] + red[1][m][c] + red[2][m][c] + red[3][m][c];
+    __hip_atomic_store(&part[size_t(m) * p.N + n], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // Every lane's device-coherent stores are complete before the ticket is taken.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned old = __hip_atomic_fetch_add(&p.ticket[tile], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old == unsigned(p.KS - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  for (int e = tid; e < rows * SK_COLS; e += 256) {
+    const int m = e / SK_COLS, c = e % SK_COLS, n = n0 + c;
+    if (n >= p.N) continue;
+    float s = 0.0f;
+    for (int q = 0; q < p.KS; ++q)
+      s += __hip_atomic_load(&p.part[(size_t(q) * p.M + m) * p.N + n], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    p.y[size_t(m) * p.N + n] = epilogue(m, s);
+  }
+  if (tid == 0) __hip_atomic_store(&p.ticket[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// K slices of a small-M product: enough workgroups to keep every CU streaming
+// (about 512), each wave at least one 128-wide group.
+int skinny_slices(int N, int K) {
+  const int tiles = (N + SK_COLS - 1) / SK_COLS;
+  const int G = K / SK_GROUP;
+  int ks = (512 + tiles - 1) / tiles;
+  const int cap = G / 4 > 1 ? G / 4 : 1;
+  return ks < cap ? ks : cap;
+}
+
+bool skinny_ok(int M, int N, int K, int r, const void* x, const void* w, const void* a, const void* b) {
+  const bool al = reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(w) % 16 == 0 &&
+                  (r == 0 || (reinterpret_cast<uintptr_t>(a) % 16 == 0 && reinterpret_cast<uintptr_t>(b) % 16 == 0));
+  // every operand must fit one buffer resource's 32-bit byte range
+  const bool fits = size_t(N) * K * 2 < (size_t(1) << 32) && size_t(M) * K * 2 < (size_t(1) << 32);
+  return M >= 1 && M <= 64 && K % SK_GROUP == 0 && r % 32 == 0 && al && fits;
+}
+
+void launch_skinny(const SkinnyParams& p, hipStream_t stream) {
+  const dim3 grid((p.N + SK_COLS - 1) / SK_COLS, p.KS);
+  if (p.M <= 16)
+    hipLaunchKernelGGL(skinny_kernel<1>, grid, dim3(256), 0, stream, p);
+  else if (p.M <= 32)
+    hipLaunchKernelGGL(skinny_kernel<2>, grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(skinny_kernel<4>, grid, dim3(256), 0, stream, p);
+}
+
 // Transpose of a bf16 matrix: dst [C, R] = src [R, C]^T, with source rows whose
 // mask byte is 0 written as zeros and, when scale != 1, every value scaled and
 // rounded to nearest even. 64 x 64 tiles through LDS; 16-byte loads and stores
@@ -438,24 +654,69 @@ void launch_main(const GemmParams& g, hipStream_t stream) {
     launch_cfg<CfgSquare>(g, stream);
 }
 
+// Forward workspace: [tickets (64 KB, only ever tickets, so they stay zero between
+// calls of any shape)] [T bf16 [M, r]] [small-M slice tiles fp32 [KS, M, max(N, r)]].
+constexpr size_t kTicketBytes = 65536;
+constexpr int kMaxTickets = int(kTicketBytes / 4);
+
+size_t skinny_part_bytes(int M, int N, int K, int r) {
+  int ks = skinny_slices(N, K), ks_r = r > 0 ? skinny_slices(r, K) : 1;
+  size_t big = 0;
+  if (ks > 1) big = size_t(ks) * M * N * 4;
+  if (ks_r > 1 && size_t(ks_r) * M * r * 4 > big) big = size_t(ks_r) * M * r * 4;
+  return align256(big);
+}
+
 }  // namespace
 
 size_t gemm_workspace_bytes(int M, int N, int K, int r) {
-  (void)N;
-  (void)K;
-  if (r <= 0 || M <= 0) return 256;
-  return align256(size_t(M) * r * 2);             // T
+  if (M <= 0 || N <= 0) return 256;
+  size_t n = kTicketBytes + (r > 0 ? align256(size_t(M) * r * 2) : 0);
+  if (M <= 64 && K % SK_GROUP == 0 && r % 32 == 0) n += skinny_part_bytes(M, N, K, r);
+  return n;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
+  char* ws = static_cast<char*>(a.ws);
+  unsigned* tickets = reinterpret_cast<unsigned*>(ws);
+  uint16_t* tws = reinterpret_cast<uint16_t*>(ws + kTicketBytes);
+  float* part = reinterpret_cast<float*>(ws + kTicketBytes + (a.r > 0 ? align256(size_t(a.M) * a.r * 2) : 0));
+  if (skinny_ok(a.M, a.N, a.K, a.r, a.X, a.W, a.A, a.B) && (a.N + SK_COLS - 1) / SK_COLS <= kMaxTickets) {
+    SkinnyParams p{};
+    p.M = a.M;
+    p.K = a.K;
+    p.part = part;
+    p.ticket = tickets;
+    p.x = static_cast<const uint16_t*>(a.X);
+    if (a.r > 0) {
+      // T = bf16(s * diag(mask) X A^T): the same product with A in place of W
+      p.w = static_cast<const uint16_t*>(a.A);
+      p.N = a.r;
+      p.r = 0;
+      p.KS = skinny_slices(a.r, a.K);
+      p.scale = a.scale;
+      p.mask = a.row_mask;
+      p.y = tws;
+      launch_skinny(p, stream);
+    }
+    p.w = static_cast<const uint16_t*>(a.W);
+    p.N = a.N;
+    p.r = a.r;
+    p.t = a.r > 0 ? tws : nullptr;
+    p.b = static_cast<const uint16_t*>(a.B);
+    p.KS = skinny_slices(a.N, a.K);
+    p.scale = 1.0f;
+    p.mask = nullptr;
+    p.y = static_cast<uint16_t*>(a.Y);
+    launch_skinny(p, stream);
+    return hipGetLastError();
+  }
   const uint16_t* tmat = nullptr;
   if (a.r > 0) {
-    // workspace: T bf16 [M, r]
-    uint16_t* t = static_cast<uint16_t*>(a.ws);
     launch_lora_down(static_cast<const uint16_t*>(a.X), static_cast<const uint16_t*>(a.A), a.M, a.K, a.r, a.scale,
-                     t, nullptr, stream);
-    tmat = t;
+                     tws, nullptr, stream);
+    tmat = tws;
   }
   GemmParams g{};
   g.seg[0] = Seg{static_cast<const uint16_t*>(a.X), static_cast<const uint16_t*>(a.W), a.K};

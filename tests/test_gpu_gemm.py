@@ -94,6 +94,42 @@ def test_ragged_shapes(M, K, N, r):
     _check_case(M, K, N, r, 16.0, mask)
 
 
+@pytest.mark.parametrize("M,K,N,r", [
+    (1, 128, 32, 32),          # one row, one reduction group, one column tile
+    (4, 4096, 4096, 0),        # an AR step's rows on a 4096-wide projection (frozen)
+    (4, 4096, 1024, 128),
+    (16, 2560, 2560, 64),
+    (17, 512, 100, 32),        # ragged rows and columns
+    (32, 2560, 10240, 64),     # four sequences x block 8 (looped model shapes)
+    (33, 10240, 2560, 64),
+    (64, 4096, 12288, 128),    # four sequences x block 16 (Qwen3-8B shapes)
+    (64, 12288, 4096, 128),
+    (64, 4096, 151936, 0),     # the LM head at a step's rows
+    (48, 256, 72, 96),         # reduction shorter than one slice of four waves
+])
+def test_small_m_shapes(M, K, N, r):
+    """Row counts of a decode step (M <= 64) take the weight-streaming path."""
+    mask = (np.random.default_rng(M * K + N).random(M) < 0.8).astype(np.uint8)
+    mask[0] = 0
+    print(f"small-M gated LoRA M={M} K={K} N={N} r={r}", flush=True)
+    _check_case(M, K, N, r, 16.0, mask)
+
+
+def test_small_m_alternating_shapes_share_the_workspace():
+    """The weight-streaming path's slice tickets live in the workspace and must be
+    left clear: shapes with different slice counts alternate on one workspace."""
+    shapes = [(64, 4096, 4096, 128), (16, 2560, 640, 32), (64, 1024, 96, 64), (8, 4096, 1024, 0)]
+    runs = []
+    for M, K, N, r in shapes:
+        X, W, A, B = workloads.gemm_inputs(M, K, N, r, seed=6)
+        args = [to_device(a, DEV) for a in (X, W, A, B)]
+        runs.append((args, to_device(np.ones(M, np.uint8), DEV)))
+    first = [_bits(_run(*args, mask, 2.0)) for args, mask in runs]
+    for _ in range(3):
+        for (args, mask), ref in zip(reversed(runs), reversed(first)):
+            np.testing.assert_array_equal(_bits(_run(*args, mask, 2.0)), ref)
+
+
 WORKLOAD_PROJECTIONS = [(name, i) for name in ("qwen", "looped", "stress")
                         for i in range(len(workloads.GEMM_CONFIGS[name]["projections"]))]
 
