@@ -9,13 +9,21 @@ verified draft positions per second (S * b / step time). Inputs are synthetic
 come from the library's draft sampler before the timed region.
 
 Also reported: per-kernel average durations from HIP events on the launch
-stream, the roofline fraction of the dominant kernel, the TV loss kernel on the
-self-distillation workload (8 x 4096 rows, vocabulary 151936) as a separate leg,
-verification alone at block 16 and block 8 with sampled and greedy decoding, the
-gated-LoRA backward on both projections, and the CPU oracle timed on a bounded
-sample of the same verify workload.
+stream (back-to-back calls) and medians of single calls after a 512 MB cache flush,
+the roofline fraction of the dominant kernel, near-tie counts of the verify
+decisions, the TV loss kernel on the self-distillation workload (8 x 4096 rows,
+vocabulary 151936) as a separate leg, verification alone at block 16 and block 8
+with sampled and greedy decoding, the gated-LoRA backward on both projections, the
+looped-model (64 x 8, V = 166144; seven rank-64 projections at M = 512) and
+large-batch stress (256 x 16; seven rank-128 projections at M = 4096) workloads
+with their HBM and MFMA fractions, the tiny workload's latencies, the decode step
+on full-size synthetic stacks (Qwen3-8B shapes and the looped 3B-class stack, 4
+sequences: AR step against Uno step, eager and as a HIP graph, and the looped
+stack's one-loop draft), a plain copy's bandwidth, and the CPU oracle timed on a
+bounded sample of the verify workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-tv] [--no-sweep]
+                       [--no-legs] [--no-step]
 
 Counter runs (rocprofv3 --pmc) time one kernel alone:
   python bench.py --only {verify,gemm_attn,gemm_mlp,tv,copy} --steps K
@@ -61,6 +69,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-tv", action="store_true", help="skip the TV-loss leg")
+    ap.add_argument("--no-step", action="store_true",
+                    help="skip the decode-step leg (full-size synthetic stacks, AR vs Uno step)")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the looped, stress and tiny workload legs")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the verify block-size / greedy sweep and the gated-LoRA backward leg")
     ap.add_argument("--only", choices=sorted(list(ONLY) + ["copy"]),
@@ -106,6 +118,59 @@ class KernelTimer:
 
     def clear(self):
         self.pairs = {}
+
+
+def median_us_flushed(fn, n, flush):
+    """Median time of n single calls, each with its own HIP event pair on the launch
+    stream, after a write of the whole `flush` buffer (512 MB: larger than L2 and the
+    256 MB MALL together) so that every call starts with cold caches."""
+    import statistics
+    import torch
+    times = []
+    for _ in range(n):
+        flush.zero_()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        times.append((s, e))
+    torch.cuda.synchronize()
+    return statistics.median(s.elapsed_time(e) for s, e in times) * 1000.0
+
+
+def near_tie_counts(diag, accept_len, b):
+    """Slots whose decision either side may take differently in fp32 and fp64 (the HIP
+    verifier flags |u - p~/q~| < 1e-6, a top-p boundary within 1e-6 of top_p, or an
+    inverse-CDF draw within 1e-6 Z of a boundary), over all slots and over the
+    decisive ones (slot 0, the kept slots and the first rejected slot)."""
+    import torch
+    flags = diag[..., 3].to(torch.int64)
+    tie = (flags & 15) != 0
+    slot = torch.arange(b, device=diag.device).unsqueeze(0)
+    decisive = slot <= torch.clamp(accept_len.to(torch.int64), max=b - 1).unsqueeze(1)
+    return {"slots": int(tie.sum().item()), "decisive_slots": int((tie & decisive).sum().item()),
+            "of_slots": int(tie.numel())}
+
+
+def copy_bandwidth(dev, iters=20):
+    """Read+write rate of a plain 1 GiB elementwise copy (torch.neg), as context for
+    the HBM roofline."""
+    import torch
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    t = KernelTimer()
+    t.run("copy", lambda: torch.neg(src, out=dst), iters)
+    torch.cuda.synchronize()
+    ms = t.avg_ms("copy")
+    del src, dst
+    return 2.0 * COPY_BYTES / (ms * 1e6)
+
+
+def gemm_bytes(M, N, K, r):
+    # X, W, A, B read once, Y written once, the row mask read once
+    return 2.0 * (M * K + N * K + r * K + N * r + M * N) + M
 
 
 def verify_bytes(S, b, V, esize=2):
@@ -157,7 +222,7 @@ def setup_verify(uno, workloads, dev):
     def run():
         return uno.uno_verify_block(p, q, draft, seq, pos, want_slot_accept=False, want_diag=False,
                                     out=outs, **sp)
-    return run, outs, (p_np, q_np)
+    return run, outs, (p_np, q_np), (p, q, draft, seq, pos)
 
 
 def setup_gemms(uno, workloads, dev):
@@ -186,7 +251,7 @@ def run_only(args, uno, workloads, dev):
         dst = torch.empty_like(src)
         fn = lambda: torch.neg(src, out=dst)
     elif args.only == "verify":
-        fn, _, _ = setup_verify(uno, workloads, dev)
+        fn, _, _, _ = setup_verify(uno, workloads, dev)
     elif args.only == "tv":
         c = workloads.TV_CONFIG
         R, V = c["n_seq"] * c["seq_len"], c["V"]
@@ -309,7 +374,7 @@ def main():
     M, r = gcfg["M"], gcfg["r"]
 
     # --- inputs resident in HBM -------------------------------------------------
-    verify_run, outs, (p_np, q_np) = setup_verify(uno, workloads, dev)
+    verify_run, outs, (p_np, q_np), verify_inputs = setup_verify(uno, workloads, dev)
     gemms = setup_gemms(uno, workloads, dev)
     torch.cuda.synchronize()
 
@@ -350,7 +415,13 @@ def main():
         t = timer.avg_ms(name)
         kernels[name] = dict(avg_us=t * 1000, flops=flops, TFLOPs=flops / (t * 1e9),
                              mfma_frac=flops / (t * 1e9) / BF16_PEAK_TFLOPS)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    kernels["verify"]["median_us_flushed"] = median_us_flushed(verify_run, 100, flush)
+    for name, (fn, _) in gemms.items():
+        kernels[name]["median_us_flushed"] = median_us_flushed(fn, 100, flush)
     acc = outs["accept_len"].float()
+    diag_run = uno.uno_verify_block(*verify_inputs, want_slot_accept=False, want_diag=True, **sp)
+    ties = near_tie_counts(diag_run["diag"], diag_run["accept_len"], b)
     dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
     traffic = traffic_from_profile(dominant)
     if dominant == "verify":
@@ -372,6 +443,17 @@ def main():
     tv_leg = None
     if not args.no_tv:
         tv_leg = tv_benchmark(uno, workloads, dev, max(3, args.steps // 4))
+
+    legs = None
+    if not args.no_legs:
+        legs = {"looped": workload_leg(uno, workloads, "looped", dev, max(10, args.steps), flush),
+                "stress": workload_leg(uno, workloads, "stress", dev, max(10, args.steps), flush),
+                "tiny": tiny_leg(uno, workloads, dev, max(10, args.steps))}
+    del flush
+    steps_leg = None
+    if not args.no_step:
+        steps_leg = step_leg(uno, workloads, dev, max(5, args.steps // 10))
+    copy_gbps = copy_bandwidth(dev)
 
     cpu = None
     if not args.no_cpu:
@@ -398,15 +480,37 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "mean_accept_len": acc.mean().item(),
+        "near_ties": ties,
+        "copy_GBps": copy_gbps,
         "cpu_baseline": cpu,
     }
+    if legs is not None:
+        line["workloads"] = legs
+    if steps_leg is not None:
+        line["decode_step"] = steps_leg
     if sweep is not None:
         line["verify_sweep"] = sweep
     if bwd is not None:
         line["gated_lora_bwd"] = bwd
     if tv_leg is not None:
         line["tv_loss"] = tv_leg
-    print(json.dumps(line))
+    print(json.dumps(line), flush=True)
+    release(uno, dev)
+
+
+def release(uno, dev):
+    """Free every device buffer and the library's cached workspaces, then wait for the
+    device, before the interpreter's own teardown: objects that outlive main() would
+    otherwise be released by garbage collection at exit, after a profiler attached to
+    the process may already have finalised."""
+    import gc
+    import torch
+    from lossless_diffusion_drafted_amd import _lib
+    torch.cuda.synchronize(dev)
+    _lib.WORKSPACES._bufs.clear()
+    gc.collect()
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize(dev)
 
 
 def tv_benchmark(uno, workloads, dev, iters):
@@ -506,6 +610,199 @@ def verify_sweep(uno, workloads, p_np, q_np, dev, iters):
     return out
 
 
+def verify_leg(uno, workloads, name, dev, iters, flush):
+    """uno_verify_block on a whole verify workload: time per call (back to back, and the
+    median of single calls after a cache flush), HBM fraction, mean accept length and
+    near-tie counts."""
+    import numpy as np
+    import torch
+    sp = workloads.SAMPLING
+    c = workloads.VERIFY_CONFIGS[name]
+    S, b, V = c["S"], c["b"], c["V"]
+    p_np, q_np = workloads.verify_logits(name)
+    p, q = dev_tensor(p_np, dev), dev_tensor(q_np, dev)
+    del p_np, q_np
+    seq = dev_tensor(np.arange(S, dtype=np.int64), dev)
+    pos = dev_tensor(np.zeros(S, dtype=np.int64), dev)
+    draft, _ = uno.uno_draft_sample(q, seq, pos, **sp)
+    outs = dict(out_tokens=torch.empty((S, b), dtype=torch.int32, device=dev),
+                accept_len=torch.empty((S,), dtype=torch.int32, device=dev),
+                resampled=torch.empty((S,), dtype=torch.int32, device=dev))
+    fn = lambda: uno.uno_verify_block(p, q, draft, seq, pos, want_slot_accept=False, want_diag=False,
+                                      out=outs, **sp)
+    fn()
+    torch.cuda.synchronize()
+    timer = KernelTimer()
+    timer.run("v", fn, iters)
+    torch.cuda.synchronize()
+    ms = timer.avg_ms("v")
+    byts = verify_bytes(S, b, V)
+    d = uno.uno_verify_block(p, q, draft, seq, pos, want_slot_accept=False, want_diag=True, **sp)
+    out = dict(shape=f"{S} x {b} x {V} bf16", avg_us=ms * 1000,
+               median_us_flushed=median_us_flushed(fn, 50, flush), bytes=byts,
+               GBps=byts / (ms * 1e6), hbm_frac=byts / (ms * 1e6) / HBM_PEAK_GBS,
+               positions_per_s=S * b / (ms / 1000), mean_accept_len=outs["accept_len"].float().mean().item(),
+               near_ties=near_tie_counts(d["diag"], d["accept_len"], b))
+    del p, q, d
+    torch.cuda.empty_cache()
+    return out
+
+
+def gemm_leg(uno, workloads, name, dev, iters, flush):
+    """The workload's gated-LoRA projections at full shape, each timed back to back and
+    as the median of flushed single calls, with its MFMA and HBM fractions (the
+    looped and stress shapes sit near the bf16 ridge, so both are reported)."""
+    import torch
+    gcfg = workloads.GEMM_CONFIGS[name]
+    M, r = gcfg["M"], gcfg["r"]
+    mask = dev_tensor(workloads.noise_row_mask(M // gcfg["b"], gcfg["b"]), dev)
+    out, total_us, total_flops = {}, 0.0, 0.0
+    for gi, (pname, K, N) in enumerate(gcfg["projections"]):
+        X, W, A, B = (dev_tensor(a, dev) for a in workloads.gemm_inputs(M, K, N, r, tag=gi))
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        fn = lambda: uno.uno_gated_lora_linear(X, W, A, B, mask, 1.0, out=Y)
+        fn()
+        torch.cuda.synchronize()
+        timer = KernelTimer()
+        timer.run("g", fn, iters)
+        torch.cuda.synchronize()
+        ms = timer.avg_ms("g")
+        flops = 2.0 * M * N * K + 2.0 * M * K * r + 2.0 * M * r * N
+        byts = gemm_bytes(M, N, K, r)
+        out[pname] = dict(K=K, N=N, avg_us=ms * 1000, median_us_flushed=median_us_flushed(fn, 50, flush),
+                          flops=flops, TFLOPs=flops / (ms * 1e9),
+                          mfma_frac=flops / (ms * 1e9) / BF16_PEAK_TFLOPS, bytes=byts,
+                          GBps=byts / (ms * 1e6), hbm_frac=byts / (ms * 1e6) / HBM_PEAK_GBS)
+        total_us += ms * 1000
+        total_flops += flops
+        del X, W, A, B, Y
+    torch.cuda.empty_cache()
+    out["all_projections"] = dict(M=M, r=r, avg_us=total_us, TFLOPs=total_flops / (total_us * 1e6),
+                                  mfma_frac=total_flops / (total_us * 1e6) / BF16_PEAK_TFLOPS)
+    return out
+
+
+def workload_leg(uno, workloads, name, dev, iters, flush):
+    leg = {"verify": verify_leg(uno, workloads, name, dev, iters, flush),
+           "gated_lora": gemm_leg(uno, workloads, name, dev, iters, flush)}
+    if name == "looped":
+        # every gated projection runs on each of 22 layers, twice (two loops) per forward
+        leg["gated_lora"]["per_forward_us"] = 44 * leg["gated_lora"]["all_projections"]["avg_us"]
+    return leg
+
+
+def tiny_leg(uno, workloads, dev, iters):
+    """Latency of each entry point on the tiny workload (one sequence, block 8, V = 1024
+    fp32; an 8 x 256 -> 256 gated LoRA of rank 16): back-to-back calls, so the figure
+    is launch and on-chip latency, not bandwidth."""
+    import numpy as np
+    import torch
+    sp = workloads.SAMPLING
+    p_np, q_np = workloads.verify_logits("tiny")
+    S = p_np.shape[0]
+    p, q = dev_tensor(p_np, dev), dev_tensor(q_np, dev)
+    seq = dev_tensor(np.arange(S, dtype=np.int64), dev)
+    pos = dev_tensor(np.zeros(S, dtype=np.int64), dev)
+    draft, _ = uno.uno_draft_sample(q, seq, pos, **sp)
+    c = workloads.GEMM_CONFIGS["tiny"]
+    (_, K, N), = c["projections"]
+    X, W, A, B = (dev_tensor(a, dev) for a in workloads.gemm_inputs(c["M"], K, N, c["r"]))
+    mask = dev_tensor(workloads.noise_row_mask(c["M"] // c["b"], c["b"]), dev)
+    fns = {"verify": lambda: uno.uno_verify_block(p, q, draft, seq, pos, want_slot_accept=False,
+                                                  want_diag=False, **sp),
+           "draft_sample": lambda: uno.uno_draft_sample(q, seq, pos, want_flags=False, **sp),
+           "gated_lora": lambda: uno.uno_gated_lora_linear(X, W, A, B, mask, 1.0)}
+    out = {}
+    for k, fn in fns.items():
+        fn()
+        torch.cuda.synchronize()
+        timer = KernelTimer()
+        timer.run(k, fn, iters)
+        torch.cuda.synchronize()
+        out[k] = dict(avg_us=timer.avg_ms(k) * 1000)
+    return out
+
+
+def _graph_ms(fn, iters):
+    """Average time of `iters` replays of a HIP graph of one call of fn (workspaces
+    are made by a warm-up call on the capture stream first)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    t = KernelTimer()
+    t.run("g", g.replay, iters)
+    torch.cuda.synchronize()
+    ms = t.avg_ms("g")
+    del g
+    return ms
+
+
+def step_leg(uno, workloads, dev, iters):
+    """The decode step on full-size synthetic stacks at 4 sequences: an AR step (one
+    frozen forward of 4 rows and the AR draw) against an Uno step (a gated draft
+    forward of the 4 blocks, the draft sampler, a frozen verify forward, verify),
+    eager (every kernel launched from the host per step) and replayed from a HIP
+    graph. The looped stack also drafts with one loop instead of two. Weight bytes
+    per forward: every projection and the LM head read once per loop."""
+    import torch
+    sp = workloads.SAMPLING
+    out = {}
+    for name in ("qwen", "looped"):
+        c = workloads.STEP_CONFIGS[name]
+        m = workloads.step_model_torch(name, dev)
+        model = uno.Model(m["embed"], m["lm_head"], m["weights"], m["lora_a"], m["lora_b"], kv_width=c["kv_width"],
+                          head_dim=c["head_dim"], lora_scale=m["lora_scale"])
+        S, b, L, V, H = c["S"], c["b"], c["loops"], c["vocab"], c["hidden"]
+        g = torch.Generator(device=dev)
+        g.manual_seed(5)
+        seed_tok = torch.randint(0, V, (S,), generator=g, device=dev, dtype=torch.int32)
+        seq = torch.arange(S, dtype=torch.int64, device=dev)
+        pos = torch.full((S,), 100, dtype=torch.int64, device=dev)
+        ar_out = {"out_tokens": torch.empty((S,), dtype=torch.int32, device=dev)}
+        st_out = {k: torch.empty((S, b) if k in ("out_tokens", "draft_tokens") else (S,), dtype=torch.int32,
+                                 device=dev) for k in ("out_tokens", "accept_len", "resampled", "draft_tokens")}
+        variants = {"ar": lambda: uno.uno_ar_step(model, seed_tok, seq, pos, loops=L, out=ar_out, **sp),
+                    "uno": lambda: uno.uno_decode_step(model, b, seed_tok, seq, pos, draft_loops=L,
+                                                       verify_loops=L, out=st_out, **sp)}
+        if L > 1:
+            variants["uno_one_loop_draft"] = lambda: uno.uno_decode_step(model, b, seed_tok, seq, pos, draft_loops=1,
+                                                                         verify_loops=L, out=st_out, **sp)
+        res = {}
+        for k, fn in variants.items():
+            fn()
+            torch.cuda.synchronize()
+            t = KernelTimer()
+            t.run(k, fn, iters)
+            torch.cuda.synchronize()
+            res[k] = dict(eager_ms=t.avg_ms(k), graph_ms=_graph_ms(fn, iters))
+        per_layer = sum(o * i for o, i in workloads.step_proj_dims(c))
+        wbytes = 2.0 * (L * c["layers"] * per_layer + V * H)
+        ar_ms = res["ar"]["graph_ms"]
+        leg = dict(shape=f"{c['layers']} layers x {L} loop(s), hidden {H}, FFN {c['ffn']}, V {V}, rank {c['rank']}, "
+                         f"{S} sequences, block {b}",
+                   weight_bytes_per_forward=wbytes, steps=res,
+                   uno_over_ar_graph=res["uno"]["graph_ms"] / ar_ms,
+                   uno_over_ar_eager=res["uno"]["eager_ms"] / res["ar"]["eager_ms"],
+                   ar_forward_GBps=wbytes / (ar_ms * 1e6), ar_forward_hbm_frac=wbytes / (ar_ms * 1e6) / HBM_PEAK_GBS,
+                   mean_accept_len=st_out["accept_len"].float().mean().item())
+        if L > 1:
+            leg["one_loop_draft_over_ar_graph"] = res["uno_one_loop_draft"]["graph_ms"] / ar_ms
+        out[name] = leg
+        del model, m
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(p_np, q_np, sp, S, b, min_seconds):
     """The fp64 CPU oracle on the same verify workload (the whole 64-sequence block,
     repeated until min_seconds of CPU time), in positions per second."""
@@ -522,9 +819,17 @@ def cpu_baseline(p_np, q_np, sp, S, b, min_seconds):
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
+    blas = None
+    try:
+        import threadpoolctl
+        blas = [dict(api=i.get("internal_api"), threads=i.get("num_threads"))
+                for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+    except ImportError:
+        pass
     return {"value": reps * S * b / el, "unit": "positions/s", "cores": 1, "kind": "oracle",
             "sample": f"full verify workload (64 x 16 slots, V=151936) x {reps} repeats, "
-                      f"{el:.1f} s, single-threaded numpy fp64"}
+                      f"{el:.1f} s, single-threaded numpy fp64",
+            "host_cpu_count": os.cpu_count(), "blas_threads": blas}
 
 
 if __name__ == "__main__":

@@ -235,6 +235,94 @@ int uno_gated_lora_linear_bwd(const void* dY, const void* X, const void* W, cons
                               void* dX, void* dA, void* dB, int M, int N, int K, int r,
                               void* workspace, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * The Uno decode step on a synthetic decoder stack ("LoopUno", "How it works":
+ * each step drafts a block of positions in one forward with the adapter on for
+ * the noise positions only, then the unmodified model verifies them and keeps the
+ * longest correct prefix, the first position always being the exact AR token;
+ * "Setup / Recipe": gated LoRA on all seven projections, and the looped model runs
+ * its layers twice per token, "Limits and next steps": drafting with one loop
+ * instead of two; "Uno Qwen3-8B" model card, "Evaluation protocol": the noise
+ * mode is random_uniform).
+ *
+ * The stack: h = embed[token]; per layer (all `loops` times, weights shared):
+ *   x = rmsnorm(h); q = G_q(x); k = G_k(x); v = G_v(x);
+ *   a = attention over a one-token context (each row attends to itself only, so
+ *       query head j returns the value of its kv head, j / (query heads / kv heads));
+ *   h = h + G_o(a); x = rmsnorm(h); h = h + G_down(silu(G_gate(x)) * G_up(x));
+ * then logits = rmsnorm(h) lm_head^T in fp32. G is the row-gated LoRA linear
+ * (uno_gated_lora_linear) with the step's row mask; rmsnorm has unit gain and
+ * eps 1e-6; activations are stored in bf16, norms, residual adds and SiLU are
+ * computed in fp32. The model's attention is a stand-in: a real model's attention
+ * over the context is not part of this library.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int hidden;        /* H, a multiple of 128                                        */
+  int kv_width;      /* width of k and v (kv heads x head_dim)                      */
+  int head_dim;      /* a multiple of 8 dividing H and kv_width; the kv heads must  */
+                     /* divide the H / head_dim query heads                         */
+  int ffn;           /* F, a multiple of 128                                        */
+  int vocab;         /* V                                                            */
+  int layers;        /* L                                                            */
+  int rank;          /* r of the gated adapter, a multiple of 32 (0: no adapter)    */
+  float lora_scale;  /* s = alpha / r                                                */
+  const void* embed;    /* bf16 [V, H]                                               */
+  const void* lm_head;  /* bf16 [V, H]                                               */
+  /* HOST arrays of 7 L DEVICE pointers, layer-major, in the order q, k, v, o, gate,
+   * up, down. weights: nn.Linear layout [out, in] (q, o [H, H]; k, v [kv_width, H];
+   * gate, up [F, H]; down [H, F]); lora_a: [r, in]; lora_b: [out, r] (both may be
+   * NULL when rank == 0). The arrays are read during the call only. */
+  const void* const* weights;
+  const void* const* lora_a;
+  const void* const* lora_b;
+} uno_model;
+
+/* One forward of M rows (1 <= M <= 64): tokens int32 [M] (device), row_mask uint8
+ * [M] (device; 1 = adapter on; NULL = frozen weights on every row), the layer stack
+ * run `loops` >= 1 times, logits fp32 [M, V] (out). Every product takes the
+ * weight-streaming path of uno_gated_lora_linear. Workspace: >= the size
+ * uno_forward_workspace returns (0 for an invalid model), zeroed once.
+ * UNO_ERR_UNSUPPORTED for shapes outside the limits above. */
+size_t uno_forward_workspace(const uno_model* model, int M);
+int uno_forward(const uno_model* model, const int32_t* tokens, const uint8_t* row_mask, int M, int loops,
+                float* logits, void* workspace, size_t ws_bytes, void* stream);
+
+/* One Uno decode step of S sequences with blocks of b rows (S * b <= 64):
+ *  1. block rows [seed_tokens[s], n_1 .. n_{b-1}]: noise token n_i is
+ *     ((w >> 40) * V) >> 24 for Philox-4x64-10 word 0 at key (sp.seed, seq_ids[s]),
+ *     counter (pos_offsets[s] + i, 2, 0, 0) (random_uniform noise);
+ *  2. draft forward of the S * b rows, `draft_loops` loops, adapter on rows 1..b-1;
+ *  3. draft tokens d ~ q~ of those logits (uno_draft_sample);
+ *  4. verify forward of the rows [seed_tokens[s], d_1 .. d_{b-1}] with the frozen
+ *     weights, `verify_loops` loops;
+ *  5. uno_verify_block with p = the verify logits, q = the draft logits.
+ * out_tokens int32 [S, b], accept_len int32 [S] and resampled int32 [S] as for
+ * uno_verify_block (accept_len and resampled may be NULL). Optional outputs:
+ * draft_tokens int32 [S, b], draft_logits and verify_logits fp32 [S * b, V] (the
+ * step then writes its logits there instead of the workspace). The workspace
+ * (>= uno_decode_step_workspace, zeroed once) begins with counter areas that each
+ * call leaves zero, so one workspace serves calls of any shape. Every kernel runs
+ * on `stream`, and the call makes no allocation and no synchronisation, so it can
+ * be recorded into a HIP graph. Limits: 1 <= b <= 64, S * b <= 64, loops >= 1. */
+size_t uno_decode_step_workspace(const uno_model* model, int S, int b);
+int uno_decode_step(const uno_model* model, int S, int b, int draft_loops, int verify_loops,
+                    uno_sampling_params sp, const int32_t* seed_tokens, const int64_t* seq_ids,
+                    const int64_t* pos_offsets, int32_t* out_tokens, int32_t* accept_len, int32_t* resampled,
+                    int32_t* draft_tokens, float* draft_logits, float* verify_logits,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/* One autoregressive step of S sequences (1 <= S <= 64): a frozen forward of the
+ * rows tokens[s] (`loops` loops), then the AR token out_tokens[s] = the inverse CDF
+ * of the filtered distribution at u_res of (sp.seed, seq_ids[s]; pos_offsets[s], 0,
+ * 0, 0): the same draw as slot 0 of uno_verify_block, so it equals out_tokens[s, 0]
+ * of a decode step with the same seed token, sequence id and position.
+ * logits fp32 [S, V] (optional out). Workspace: >= uno_ar_step_workspace, zeroed
+ * once. */
+size_t uno_ar_step_workspace(const uno_model* model, int S);
+int uno_ar_step(const uno_model* model, int S, int loops, uno_sampling_params sp, const int32_t* tokens,
+                const int64_t* seq_ids, const int64_t* pos_offsets, int32_t* out_tokens, float* logits,
+                void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

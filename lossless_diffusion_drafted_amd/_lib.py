@@ -35,6 +35,8 @@ EXPORTS = [
     "uno_tv_loss_workspace", "uno_tv_loss_fwd_bwd",
     "uno_gated_lora_linear_workspace", "uno_gated_lora_linear",
     "uno_gated_lora_linear_bwd_workspace", "uno_gated_lora_linear_bwd",
+    "uno_forward_workspace", "uno_forward", "uno_decode_step_workspace", "uno_decode_step",
+    "uno_ar_step_workspace", "uno_ar_step",
 ]
 
 
@@ -42,6 +44,16 @@ class SamplingParams(ctypes.Structure):
     """uno_sampling_params (include/uno.h)."""
     _fields_ = [("temperature", ctypes.c_double), ("top_p", ctypes.c_double),
                 ("top_k", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+class UnoModel(ctypes.Structure):
+    """uno_model (include/uno.h)."""
+    _fields_ = [("hidden", ctypes.c_int), ("kv_width", ctypes.c_int), ("head_dim", ctypes.c_int),
+                ("ffn", ctypes.c_int), ("vocab", ctypes.c_int), ("layers", ctypes.c_int),
+                ("rank", ctypes.c_int), ("lora_scale", ctypes.c_float),
+                ("embed", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
+                ("weights", ctypes.POINTER(ctypes.c_void_p)), ("lora_a", ctypes.POINTER(ctypes.c_void_p)),
+                ("lora_b", ctypes.POINTER(ctypes.c_void_p))]
 
 
 class UnoError(RuntimeError):
@@ -89,6 +101,13 @@ def load():
             "uno_gated_lora_linear_bwd_workspace": (_SZ, [_I, _I, _I, _I]),
             "uno_gated_lora_linear_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _I,
                                                _I, _I, _I, _P, _SZ, _P]),
+            "uno_forward_workspace": (_SZ, [_P, _I]),
+            "uno_forward": (_I, [_P, _P, _P, _I, _I, _P, _P, _SZ, _P]),
+            "uno_decode_step_workspace": (_SZ, [_P, _I, _I]),
+            "uno_decode_step": (_I, [_P, _I, _I, _I, _I, SamplingParams, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     _P, _SZ, _P]),
+            "uno_ar_step_workspace": (_SZ, [_P, _I]),
+            "uno_ar_step": (_I, [_P, _I, _I, SamplingParams, _P, _P, _P, _P, _P, _P, _SZ, _P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libuno.so")
 
-SOURCES = ["api.cpp", "verify.hip", "tv.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "verify.hip", "tv.hip", "gemm.hip", "model.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

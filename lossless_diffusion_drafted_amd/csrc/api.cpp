@@ -330,3 +330,149 @@ int uno_gated_lora_linear_bwd(const void* dY, const void* X, const void* W, cons
 }
 
 }  // extern "C"
+
+namespace {
+
+// The model description and its checks, shared by the forward and step entry points.
+int model_desc(const uno_model* m, int M, const char* fn, uno::ModelDesc* md) {
+  if (!m) return fail(UNO_ERR_INVALID_ARG, "%s: model is null", fn);
+  if (!m->embed || !m->lm_head || (m->layers > 0 && !m->weights))
+    return fail(UNO_ERR_INVALID_ARG, "%s: a model weight pointer is null", fn);
+  if (m->rank > 0 && m->layers > 0 && (!m->lora_a || !m->lora_b))
+    return fail(UNO_ERR_INVALID_ARG, "%s: rank %d given without adapter pointers", fn, m->rank);
+  for (int i = 0; i < 7 * m->layers; ++i) {
+    if (!m->weights[i]) return fail(UNO_ERR_INVALID_ARG, "%s: weight %d is null", fn, i);
+    if (m->rank > 0 && (!m->lora_a[i] || !m->lora_b[i]))
+      return fail(UNO_ERR_INVALID_ARG, "%s: adapter factor %d is null", fn, i);
+  }
+  md->hidden = m->hidden;
+  md->kv_width = m->kv_width;
+  md->head_dim = m->head_dim;
+  md->ffn = m->ffn;
+  md->vocab = m->vocab;
+  md->layers = m->layers;
+  md->rank = m->rank;
+  md->lora_scale = m->lora_scale;
+  md->embed = m->embed;
+  md->lm_head = m->lm_head;
+  md->w = m->weights;
+  md->lora_a = m->lora_a;
+  md->lora_b = m->lora_b;
+  const size_t lim = size_t(1) << 32;
+  if (size_t(m->vocab) * m->hidden * 2 >= lim || size_t(m->ffn) * m->hidden * 2 >= lim)
+    return fail(UNO_ERR_UNSUPPORTED, "%s: a weight matrix of 4 GiB or more", fn);
+  const int c = uno::model_check(*md, M);
+  if (c == 1)
+    return fail(UNO_ERR_UNSUPPORTED,
+                "%s: unsupported model shape (hidden %d, kv_width %d, head_dim %d, ffn %d, rank %d): hidden and "
+                "ffn must be multiples of 128, rank of 32, head_dim of 8 and divide hidden and kv_width, and the "
+                "kv heads divide the query heads", fn, m->hidden, m->kv_width, m->head_dim, m->ffn, m->rank);
+  if (c == 2) return fail(UNO_ERR_UNSUPPORTED, "%s: %d rows; a forward takes 1 to 64", fn, M);
+  return UNO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t uno_forward_workspace(const uno_model* model, int M) {
+  uno::ModelDesc md;
+  if (model_desc(model, M, "uno_forward_workspace", &md) != UNO_OK) return 0;
+  return uno::forward_workspace_bytes(md, M);
+}
+
+int uno_forward(const uno_model* model, const int32_t* tokens, const uint8_t* row_mask, int M, int loops,
+                float* logits, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "uno_forward";
+  uno::ModelDesc md;
+  int st = model_desc(model, M, fn, &md);
+  if (st != UNO_OK) return st;
+  if (loops < 1) return fail(UNO_ERR_INVALID_ARG, "%s: loops = %d < 1", fn, loops);
+  if (!tokens || !logits) return fail(UNO_ERR_INVALID_ARG, "%s: a required pointer is null", fn);
+  const size_t need = uno::forward_workspace_bytes(md, M);
+  if (!workspace || ws_bytes < need)
+    return fail(UNO_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, need);
+  return hip_status(uno::launch_forward(md, tokens, row_mask, M, loops, logits, workspace,
+                                        static_cast<hipStream_t>(stream)), "uno_forward launch");
+}
+
+size_t uno_decode_step_workspace(const uno_model* model, int S, int b) {
+  uno::ModelDesc md;
+  if (S < 1 || b < 1 || S * b > 64) return 0;
+  if (model_desc(model, S * b, "uno_decode_step_workspace", &md) != UNO_OK) return 0;
+  return uno::step_workspace_bytes(md, S, b);
+}
+
+int uno_decode_step(const uno_model* model, int S, int b, int draft_loops, int verify_loops,
+                    uno_sampling_params sp, const int32_t* seed_tokens, const int64_t* seq_ids,
+                    const int64_t* pos_offsets, int32_t* out_tokens, int32_t* accept_len, int32_t* resampled,
+                    int32_t* draft_tokens, float* draft_logits, float* verify_logits,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "uno_decode_step";
+  int st = check_sampling(sp, S, b, 1, fn);
+  if (st != UNO_OK) return st;
+  if (S < 1 || (long long)S * b > 64)
+    return fail(UNO_ERR_UNSUPPORTED, "%s: S = %d blocks of b = %d rows; a step takes 1 to 64 rows", fn, S, b);
+  uno::ModelDesc md;
+  if ((st = model_desc(model, S * b, fn, &md)) != UNO_OK) return st;
+  if (draft_loops < 1 || verify_loops < 1)
+    return fail(UNO_ERR_INVALID_ARG, "%s: loops must be >= 1 (draft %d, verify %d)", fn, draft_loops, verify_loops);
+  if (!seed_tokens || !seq_ids || !pos_offsets || !out_tokens)
+    return fail(UNO_ERR_INVALID_ARG, "%s: a required pointer is null", fn);
+  const size_t need = uno::step_workspace_bytes(md, S, b);
+  if (!workspace || ws_bytes < need)
+    return fail(UNO_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, need);
+  uno::StepArgs a{};
+  a.S = S;
+  a.b = b;
+  a.draft_loops = draft_loops;
+  a.verify_loops = verify_loops;
+  a.sp = to_args(sp);
+  a.seed_tokens = seed_tokens;
+  a.seq_ids = seq_ids;
+  a.pos = pos_offsets;
+  a.out_tokens = out_tokens;
+  a.accept_len = accept_len;
+  a.resampled = resampled;
+  a.drafts = draft_tokens;
+  a.draft_logits = draft_logits;
+  a.verify_logits = verify_logits;
+  a.ws = workspace;
+  return hip_status(uno::launch_decode_step(md, a, static_cast<hipStream_t>(stream)), "uno_decode_step launch");
+}
+
+size_t uno_ar_step_workspace(const uno_model* model, int S) {
+  uno::ModelDesc md;
+  if (model_desc(model, S, "uno_ar_step_workspace", &md) != UNO_OK) return 0;
+  return uno::ar_step_workspace_bytes(md, S);
+}
+
+int uno_ar_step(const uno_model* model, int S, int loops, uno_sampling_params sp, const int32_t* tokens,
+                const int64_t* seq_ids, const int64_t* pos_offsets, int32_t* out_tokens, float* logits,
+                void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "uno_ar_step";
+  int st = check_sampling(sp, S, 1, 1, fn);
+  if (st != UNO_OK) return st;
+  uno::ModelDesc md;
+  if ((st = model_desc(model, S, fn, &md)) != UNO_OK) return st;
+  if (loops < 1) return fail(UNO_ERR_INVALID_ARG, "%s: loops = %d < 1", fn, loops);
+  if (!tokens || !seq_ids || !pos_offsets || !out_tokens)
+    return fail(UNO_ERR_INVALID_ARG, "%s: a required pointer is null", fn);
+  const size_t need = uno::ar_step_workspace_bytes(md, S);
+  if (!workspace || ws_bytes < need)
+    return fail(UNO_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn, ws_bytes, need);
+  uno::StepArgs a{};
+  a.S = S;
+  a.b = 1;
+  a.draft_loops = loops;
+  a.verify_loops = loops;
+  a.sp = to_args(sp);
+  a.seed_tokens = tokens;
+  a.seq_ids = seq_ids;
+  a.pos = pos_offsets;
+  a.out_tokens = out_tokens;
+  a.verify_logits = logits;
+  a.ws = workspace;
+  return hip_status(uno::launch_ar_step(md, a, static_cast<hipStream_t>(stream)), "uno_ar_step launch");
+}
+}  // extern "C"

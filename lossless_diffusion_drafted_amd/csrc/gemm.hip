@@ -348,17 +348,21 @@ __global__ __launch_bounds__(LD_WAVES * 64) void lora_down_kernel(const uint16_t
 // Each workgroup owns 32 output columns and one of KS slices of the reduction;
 // its four waves split the slice into contiguous runs of 128-wide groups. A wave
 // multiplies its 32 W rows (two 16-column blocks) against every X row with
-// v_mfma_f32_16x16x32_bf16, M padded to 16-row blocks.
-//   The reduction index of each MFMA is permuted the same way on both operands:
-// in a 128-wide group, lane group g (lanes 16 g .. 16 g + 15) covers k = 32 g ..
-// 32 g + 31 and feeds 8 of them to each of the group's four MFMAs. Each lane's W
-// and X loads are therefore 64 contiguous bytes, and a W row is read in 256-byte
-// runs. The delta segment [T | B] (r more reduction steps, T already scaled and
+// v_mfma_f32_16x16x32_bf16, M padded to 16-row blocks, in the instruction's own
+// operand layout: for the c-th 32-wide step of a group, lane group g (lanes 16 g ..
+// 16 g + 15) holds k = 32 c + 8 g .. + 7, so each load instruction reads 64
+// contiguous bytes of each of 16 rows and a group reads 256-byte runs of every row.
+// (Measured: a layout with 64 contiguous bytes per lane instead, spread over four
+// instructions, streamed W 1.3 to 1.6 times slower.) The next group's loads are in
+// flight while a group is multiplied; deeper prefetch measured slower (fewer waves
+// fit). The delta segment [T | B] (r more reduction steps, T already scaled and
 // gated) is taken 32 wide by the tile's last wave.
 //   The four wave partials meet in LDS in wave order. With KS > 1 each slice
-// stores its fp32 tile with device-coherent stores and takes a ticket; the last
-// slice of a column tile to finish adds the KS tiles in slice order (so the sum
-// order is fixed), writes bf16 and resets the ticket.
+// stores its fp32 tile with device-coherent stores and takes a ticket (relaxed:
+// the stores are complete and coherent before it; an acquire-release ticket, which
+// writes back and invalidates L2, measured up to 3 times slower); the last slice
+// of a column tile to finish adds the KS tiles in slice order (so the sum order is
+// fixed), writes the output and resets the ticket.
 struct SkinnyParams {
   const uint16_t* x;      // [M, K]
   const uint16_t* w;      // [N, K]
@@ -368,6 +372,7 @@ struct SkinnyParams {
   float scale;            // epilogue: y = mask[m] ? scale * acc : 0 (mask may be null)
   const uint8_t* mask;
   uint16_t* y;            // [M, N] bf16
+  float* yf;              // [M, N] fp32 instead of y when given
   float* part;            // [KS, M, N] fp32 slice tiles (KS > 1)
   unsigned* ticket;       // [ceil(N / 32)], zero on entry and on exit
 };
@@ -399,13 +404,13 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
   for (int i = 0; i < MB; ++i) {
     const int m = i * 16 + fr;
     xin[i] = m < p.M;
-    xo[i] = uint32_t((size_t(m) * p.K + fg * 32) * 2);
+    xo[i] = uint32_t((size_t(m) * p.K + fg * 8) * 2);
   }
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int n = n0 + j * 16 + fr;
     win[j] = n < p.N;
-    wo[j] = uint32_t((size_t(n) * p.K + fg * 32) * 2);
+    wo[j] = uint32_t((size_t(n) * p.K + fg * 8) * 2);
   }
 
   f32x4_t acc[MB][NB];
@@ -415,19 +420,23 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   u32x4_t xa[MB][4], wa[NB][4], xb[MB][4], wb[NB][4];
+  // Group g's loads; past the wave's last group they read out of range (zeros), so
+  // every call issues the same loads and the waits are counted at compile time.
   auto load = [&](int g, u32x4_t (&xv)[MB][4], u32x4_t (&wv)[NB][4]) {
     const uint32_t kb = uint32_t(g) * SK_GROUP * 2;
+    const bool live = g < g1;
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        wv[j][c] = __builtin_amdgcn_raw_buffer_load_b128(rw, win[j] ? wo[j] + kb + c * 16 : kOutOfRange, 0u,
-                                                         kBufNonTemporal);
+        wv[j][c] = __builtin_amdgcn_raw_buffer_load_b128(rw, (live && win[j]) ? wo[j] + kb + c * 64 : kOutOfRange,
+                                                         0u, kBufNonTemporal);
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        xv[i][c] = __builtin_amdgcn_raw_buffer_load_b128(rx, xin[i] ? xo[i] + kb + c * 16 : kOutOfRange, 0u, 0);
+        xv[i][c] = __builtin_amdgcn_raw_buffer_load_b128(rx, (live && xin[i]) ? xo[i] + kb + c * 64 : kOutOfRange,
+                                                         0u, 0);
   };
   auto mma = [&](const u32x4_t (&xv)[MB][4], const u32x4_t (&wv)[NB][4]) {
 #pragma unroll
@@ -442,14 +451,12 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
   };
   // Two register sets, so every index is a constant: the next group's loads are in
   // flight while the current group is multiplied.
-  if (g0 < g1) load(g0, xa, wa);
+  load(g0, xa, wa);
   for (int g = g0; g < g1; g += 2) {
-    if (g + 1 < g1) load(g + 1, xb, wb);
+    load(g + 1, xb, wb);
     mma(xa, wa);
-    if (g + 1 < g1) {
-      if (g + 2 < g1) load(g + 2, xa, wa);
-      mma(xb, wb);
-    }
+    load(g + 2, xa, wa);
+    if (g + 1 < g1) mma(xb, wb);
   }
 
   // Delta segment: r more reduction steps, 32 wide, on the tile's last wave.
@@ -489,17 +496,19 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
       for (int v = 0; v < 4; ++v) red[wave][i * 16 + 4 * fg + v][j * 16 + fr] = acc[i][j][v];
   __syncthreads();
 
-  auto epilogue = [&](int m, float s) -> uint16_t {
+  auto store = [&](int m, int n, float s) {
     const float y = (p.mask && p.mask[m] == 0) ? 0.0f : p.scale * s;
-    return __builtin_bit_cast(uint16_t, (__bf16)y);
+    if (p.yf)
+      p.yf[size_t(m) * p.N + n] = y;
+    else
+      p.y[size_t(m) * p.N + n] = __builtin_bit_cast(uint16_t, (__bf16)y);
   };
   const int rows = p.M < ROWS ? p.M : ROWS;
   if (p.KS == 1) {
     for (int e = tid; e < rows * SK_COLS; e += 256) {
       const int m = e / SK_COLS, c = e % SK_COLS, n = n0 + c;
       if (n >= p.N) continue;
-      const float s = red[0][m][c] + red[1][m][c] + red[2][m][c] + red[3][m][c];
-      p.y[size_t(m) * p.N + n] = epilogue(m, s);
+      store(m, n, red[0][m][c] + red[1][m][c] + red[2][m][c] + red[3][m][c]);
     }
     return;
   }
@@ -514,7 +523,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const unsigned old = __hip_atomic_fetch_add(&p.ticket[tile], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned old = __hip_atomic_fetch_add(&p.ticket[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = old == unsigned(p.KS - 1) ? 1 : 0;
   }
   __syncthreads();
@@ -525,17 +534,17 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
     float s = 0.0f;
     for (int q = 0; q < p.KS; ++q)
       s += __hip_atomic_load(&p.part[(size_t(q) * p.M + m) * p.N + n], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    p.y[size_t(m) * p.N + n] = epilogue(m, s);
+    store(m, n, s);
   }
   if (tid == 0) __hip_atomic_store(&p.ticket[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// K slices of a small-M product: enough workgroups to keep every CU streaming
-// (about 512), each wave at least one 128-wide group.
+// K slices of a small-M product: about one workgroup per CU (measured best
+// against 2, 4 and 8 per CU), each wave at least one 128-wide group.
 int skinny_slices(int N, int K) {
   const int tiles = (N + SK_COLS - 1) / SK_COLS;
   const int G = K / SK_GROUP;
-  int ks = (512 + tiles - 1) / tiles;
+  int ks = (256 + tiles - 1) / tiles;
   const int cap = G / 4 > 1 ? G / 4 : 1;
   return ks < cap ? ks : cap;
 }
@@ -679,10 +688,17 @@ size_t gemm_workspace_bytes(int M, int N, int K, int r) {
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   char* ws = static_cast<char*>(a.ws);
-  unsigned* tickets = reinterpret_cast<unsigned*>(ws);
-  uint16_t* tws = reinterpret_cast<uint16_t*>(ws + kTicketBytes);
-  float* part = reinterpret_cast<float*>(ws + kTicketBytes + (a.r > 0 ? align256(size_t(a.M) * a.r * 2) : 0));
-  if (skinny_ok(a.M, a.N, a.K, a.r, a.X, a.W, a.A, a.B) && (a.N + SK_COLS - 1) / SK_COLS <= kMaxTickets) {
+  unsigned* tickets = a.tickets;
+  if (tickets == nullptr) {
+    tickets = reinterpret_cast<unsigned*>(ws);
+    ws += kTicketBytes;
+  }
+  uint16_t* tws = reinterpret_cast<uint16_t*>(ws);
+  float* part = reinterpret_cast<float*>(ws + (a.r > 0 ? align256(size_t(a.M) * a.r * 2) : 0));
+  const bool small = skinny_ok(a.M, a.N, a.K, a.r, a.X, a.W, a.A, a.B) &&
+                     (a.N + SK_COLS - 1) / SK_COLS <= kMaxTickets && (a.r + SK_COLS - 1) / SK_COLS <= kMaxTickets;
+  if (a.y_f32 && !small) return hipErrorInvalidValue;   // fp32 output exists on the small-M path only
+  if (small) {
     SkinnyParams p{};
     p.M = a.M;
     p.K = a.K;
@@ -708,7 +724,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     p.KS = skinny_slices(a.N, a.K);
     p.scale = 1.0f;
     p.mask = nullptr;
-    p.y = static_cast<uint16_t*>(a.Y);
+    p.y = a.y_f32 ? nullptr : static_cast<uint16_t*>(a.Y);
+    p.yf = a.y_f32 ? static_cast<float*>(a.Y) : nullptr;
     launch_skinny(p, stream);
     return hipGetLastError();
   }

@@ -65,6 +65,8 @@ struct GemmArgs {
   void* Y;
   int M, N, K, r;
   void* ws;
+  unsigned* tickets = nullptr;   // slice tickets kept apart from ws (else the first 64 KB of ws)
+  bool y_f32 = false;            // Y is fp32 (small-M path only)
 };
 
 size_t verify_workspace_bytes(int S, int b);
@@ -98,5 +100,41 @@ struct GemmBwdArgs {
 size_t gemm_bwd_workspace_bytes(int M, int N, int K, int r);
 hipError_t launch_gemm_bwd(const GemmBwdArgs& a, hipStream_t stream);
 hipError_t launch_zero(void* ptr, size_t bytes, hipStream_t stream);
+
+// Synthetic decoder stack of the decode step (csrc/model.hip).
+struct ModelDesc {
+  int hidden, kv_width, head_dim, ffn, vocab, layers, rank;
+  float lora_scale;
+  const void* embed;             // bf16 [vocab, hidden]
+  const void* lm_head;           // bf16 [vocab, hidden]
+  const void* const* w;          // host array [layers * 7]: q, k, v, o, gate, up, down
+  const void* const* lora_a;     // host array [layers * 7] (rank > 0)
+  const void* const* lora_b;
+};
+
+struct StepArgs {
+  int S, b, draft_loops, verify_loops;
+  SamplingArgs sp;
+  const int32_t* seed_tokens;    // [S]
+  const int64_t* seq_ids;        // [S]
+  const int64_t* pos;            // [S]
+  int32_t* out_tokens;           // [S, b]
+  int32_t* accept_len;           // [S] (optional)
+  int32_t* resampled;            // [S] (optional)
+  int32_t* drafts;               // [S, b] (optional)
+  float* draft_logits;           // [S * b, vocab] (optional)
+  float* verify_logits;          // [S * b, vocab] (optional)
+  void* ws;
+};
+
+// 0 = valid; 1 = the model's shapes are not supported; 2 = M outside [1, 64].
+int model_check(const ModelDesc& md, int M);
+size_t forward_workspace_bytes(const ModelDesc& md, int M);
+hipError_t launch_forward(const ModelDesc& md, const int32_t* tokens, const uint8_t* mask, int M, int loops,
+                          float* logits, void* ws, hipStream_t stream);
+size_t step_workspace_bytes(const ModelDesc& md, int S, int b);
+hipError_t launch_decode_step(const ModelDesc& md, const StepArgs& a, hipStream_t stream);
+size_t ar_step_workspace_bytes(const ModelDesc& md, int S);
+hipError_t launch_ar_step(const ModelDesc& md, const StepArgs& a, hipStream_t stream);
 
 }  // namespace uno

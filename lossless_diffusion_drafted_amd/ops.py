@@ -8,7 +8,9 @@ asynchronous like any other work on that stream.
 import torch
 
 from . import _lib
-from ._lib import SamplingParams, WORKSPACES, check, load, ptr, require, stream_handle
+import ctypes
+
+from ._lib import SamplingParams, UnoModel, WORKSPACES, check, load, ptr, require, stream_handle
 
 
 def sampling_params(temperature=1.0, top_k=50, top_p=0.95, seed=0):
@@ -174,3 +176,120 @@ def uno_gated_lora_linear_bwd(dY, X, W, A, B, row_mask, scale=1.0, want_dx=True,
                                        ptr(dX), ptr(dA), ptr(dB), M, N, K, r, ptr(ws), ws.numel(), stream)
     check(st, "uno_gated_lora_linear_bwd")
     return dX, dA, dB
+
+
+PROJECTIONS = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+class Model:
+    """A decoder stack for uno_forward / uno_decode_step / uno_ar_step: bf16 device
+    tensors and the uno_model description that points at them (see uno.h).
+
+    embed, lm_head: [V, H]; weights: list over layers of 7 tensors in the order of
+    PROJECTIONS, nn.Linear layout [out, in]; lora_a / lora_b: the same nesting of
+    [r, in] / [out, r] tensors, or None for no adapter."""
+
+    def __init__(self, embed, lm_head, weights, lora_a=None, lora_b=None, kv_width=None, head_dim=128,
+                 lora_scale=1.0):
+        V, H = embed.shape
+        L = len(weights)
+        F = weights[0][4].shape[0] if L else 0
+        kvw = kv_width if kv_width is not None else (weights[0][1].shape[0] if L else H)
+        r = lora_a[0][0].shape[0] if (lora_a and L) else 0
+        for t, n in ((embed, "embed"), (lm_head, "lm_head")):
+            require(t, n, dtype=torch.bfloat16, shape=(V, H))
+        flat = [t for layer in weights for t in layer]
+        for t in flat:
+            require(t, "weight", dtype=torch.bfloat16, device=embed.device)
+        self.tensors = [embed, lm_head] + flat
+        self._w = (ctypes.c_void_p * max(1, len(flat)))(*[t.data_ptr() for t in flat])
+        self._a = self._b = None
+        if r:
+            fa = [t for layer in lora_a for t in layer]
+            fb = [t for layer in lora_b for t in layer]
+            for t in fa + fb:
+                require(t, "adapter factor", dtype=torch.bfloat16, device=embed.device)
+            self.tensors += fa + fb
+            self._a = (ctypes.c_void_p * len(fa))(*[t.data_ptr() for t in fa])
+            self._b = (ctypes.c_void_p * len(fb))(*[t.data_ptr() for t in fb])
+        self.desc = UnoModel(H, kvw, head_dim, F, V, L, r, float(lora_scale), embed.data_ptr(),
+                             lm_head.data_ptr(), ctypes.cast(self._w, ctypes.POINTER(ctypes.c_void_p)),
+                             ctypes.cast(self._a, ctypes.POINTER(ctypes.c_void_p)) if r else None,
+                             ctypes.cast(self._b, ctypes.POINTER(ctypes.c_void_p)) if r else None)
+        self.device = embed.device
+        self.vocab, self.hidden, self.rank = V, H, r
+
+
+def uno_forward(model, tokens, row_mask=None, loops=1, logits=None):
+    """fp32 logits [M, V] of one forward of the token rows (see uno_forward in uno.h)."""
+    lib = load()
+    M = tokens.shape[0]
+    dev = model.device
+    require(tokens, "tokens", dtype=torch.int32, shape=(M,), device=dev)
+    if row_mask is not None:
+        require(row_mask, "row_mask", dtype=torch.uint8, shape=(M,), device=dev)
+    out = logits if logits is not None else torch.empty((M, model.vocab), dtype=torch.float32, device=dev)
+    require(out, "logits", dtype=torch.float32, shape=(M, model.vocab), device=dev)
+    n = lib.uno_forward_workspace(ctypes.byref(model.desc), M)   # 0: the call reports why
+    ws = WORKSPACES.get(dev, stream_handle(dev), "step", max(n, 256))
+    check(lib.uno_forward(ctypes.byref(model.desc), ptr(tokens), ptr(row_mask), M, int(loops), ptr(out),
+                          ptr(ws), ws.numel() if n else 0, stream_handle(dev)), "uno_forward")
+    return out
+
+
+def uno_decode_step(model, b, seed_tokens, seq_ids, pos_offsets, temperature=1.0, top_k=50, top_p=0.95, seed=0,
+                    draft_loops=1, verify_loops=1, want_logits=False, out=None):
+    """One Uno decode step (see uno_decode_step in uno.h). Returns a dict of device
+    tensors: out_tokens [S,b], accept_len [S], resampled [S], draft_tokens [S,b] and,
+    with want_logits, draft_logits / verify_logits [S*b, V] fp32. `out` may pass
+    preallocated tensors under the same keys (then nothing is allocated)."""
+    lib = load()
+    S = seed_tokens.shape[0]
+    dev = model.device
+    require(seed_tokens, "seed_tokens", dtype=torch.int32, shape=(S,), device=dev)
+    require(seq_ids, "seq_ids", dtype=torch.int64, shape=(S,), device=dev)
+    require(pos_offsets, "pos_offsets", dtype=torch.int64, shape=(S,), device=dev)
+    o = dict(out or {})
+    for k, shape, dt in (("out_tokens", (S, b), torch.int32), ("accept_len", (S,), torch.int32),
+                         ("resampled", (S,), torch.int32), ("draft_tokens", (S, b), torch.int32)):
+        if k not in o:
+            o[k] = torch.empty(shape, dtype=dt, device=dev)
+    if want_logits:
+        for k in ("draft_logits", "verify_logits"):
+            if k not in o:
+                o[k] = torch.empty((S * b, model.vocab), dtype=torch.float32, device=dev)
+    sp = sampling_params(temperature, top_k, top_p, seed)
+    n = lib.uno_decode_step_workspace(ctypes.byref(model.desc), S, b)
+    ws = WORKSPACES.get(dev, stream_handle(dev), "step", max(n, 256))
+    st = lib.uno_decode_step(ctypes.byref(model.desc), S, b, int(draft_loops), int(verify_loops), sp,
+                             ptr(seed_tokens), ptr(seq_ids), ptr(pos_offsets), ptr(o["out_tokens"]),
+                             ptr(o["accept_len"]), ptr(o["resampled"]), ptr(o["draft_tokens"]),
+                             ptr(o.get("draft_logits")), ptr(o.get("verify_logits")), ptr(ws),
+                             ws.numel() if n else 0, stream_handle(dev))
+    check(st, "uno_decode_step")
+    return o
+
+
+def uno_ar_step(model, tokens, seq_ids, pos_offsets, temperature=1.0, top_k=50, top_p=0.95, seed=0, loops=1,
+                want_logits=False, out=None):
+    """One autoregressive step (see uno_ar_step in uno.h): returns (out_tokens [S] int32,
+    logits [S, V] fp32 or None)."""
+    lib = load()
+    S = tokens.shape[0]
+    dev = model.device
+    require(tokens, "tokens", dtype=torch.int32, shape=(S,), device=dev)
+    require(seq_ids, "seq_ids", dtype=torch.int64, shape=(S,), device=dev)
+    require(pos_offsets, "pos_offsets", dtype=torch.int64, shape=(S,), device=dev)
+    o = dict(out or {})
+    if "out_tokens" not in o:
+        o["out_tokens"] = torch.empty((S,), dtype=torch.int32, device=dev)
+    if want_logits and "logits" not in o:
+        o["logits"] = torch.empty((S, model.vocab), dtype=torch.float32, device=dev)
+    sp = sampling_params(temperature, top_k, top_p, seed)
+    n = lib.uno_ar_step_workspace(ctypes.byref(model.desc), S)
+    ws = WORKSPACES.get(dev, stream_handle(dev), "step", max(n, 256))
+    st = lib.uno_ar_step(ctypes.byref(model.desc), S, int(loops), sp, ptr(tokens), ptr(seq_ids), ptr(pos_offsets),
+                         ptr(o["out_tokens"]), ptr(o.get("logits")), ptr(ws), ws.numel() if n else 0,
+                         stream_handle(dev))
+    check(st, "uno_ar_step")
+    return o["out_tokens"], o.get("logits")

@@ -11,7 +11,7 @@ method (page titles and sections are cited in each module), pinned by the
 routines and invariants.
 """
 
-from .philox import philox4x64_10, slot_uniforms, word_to_uniform  # noqa: F401
+from .philox import noise_token, philox4x64_10, slot_uniforms, word_to_uniform  # noqa: F401
 from .sampling import (  # noqa: F401
     EVENT_Q_ZERO, EVENT_RES_ZERO, NEAR_TIE, TIE_ACCEPT, TIE_ICDF, TIE_MASK,
     TIE_TOPP_P, TIE_TOPP_Q, decode_logits, draft_sample, expected_accept_len,
@@ -19,3 +19,4 @@ from .sampling import (  # noqa: F401
 )
 from .tv import tv_loss_fwd_bwd  # noqa: F401
 from .gated_lora import bf16_bits_to_f64, gated_lora_linear, gated_lora_linear_bwd, lora_delta  # noqa: F401
+from . import step  # noqa: F401

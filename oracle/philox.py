@@ -12,6 +12,7 @@ stream, 0, 0), so every decision is reproducible from its inputs alone:
 
   * stream 0, word 0 -> u_acc (accept test), word 1 -> u_res (AR / residual draw)
   * stream 1, word 0 -> u_draft (the draft sampler's draw)
+  * stream 2, word 0 -> the noise token of a block's noise row (random_uniform)
 
 A 64-bit word w becomes u = (w >> 40) * 2**-24, a 24-bit uniform in [0, 1) that
 is exact in both fp32 and fp64.
@@ -29,6 +30,7 @@ PHILOX_W1 = 0xBB67AE8584CAA73B
 
 STREAM_VERIFY = 0
 STREAM_DRAFT = 1
+STREAM_NOISE = 2
 
 
 def _round(c, k):
@@ -63,3 +65,12 @@ def slot_uniforms(seed, seq_id, position, stream=STREAM_VERIFY):
     w = philox4x64_10((int(position) & MASK64, stream, 0, 0),
                       (int(seed) & MASK64, int(seq_id) & MASK64))
     return word_to_uniform(w[0]), word_to_uniform(w[1])
+
+
+def noise_token(seed, seq_id, position, vocab):
+    """A random_uniform noise token in [0, vocab): the top 24 bits of Philox word 0 at
+    (seed, seq_id; position, stream 2, 0, 0) scaled by the vocabulary size with
+    integer arithmetic, floor(w24 * vocab / 2^24)."""
+    w = philox4x64_10((int(position) & MASK64, STREAM_NOISE, 0, 0),
+                      (int(seed) & MASK64, int(seq_id) & MASK64))
+    return ((int(w[0]) >> 40) * int(vocab)) >> 24

@@ -195,3 +195,72 @@ def tv_inputs_torch(n_rows, V, device, seed=0, teacher_sigma=3.0, student_sigma=
         s[r0:r1] = sf.to(torch.bfloat16)
         del tf, sf
     return t, s
+
+
+# Decoder stacks of the decode step (uno_decode_step). "qwen": Qwen3-8B shapes
+# (36 layers, hidden 4096, 8 kv heads of 128, FFN 12288, vocabulary 151936), rank-128
+# adapter, block 16. "looped": the 3B-class looped stack of 22 layers run twice per
+# token (hidden 2560, every attention projection 2560 x 2560 (reading), FFN 10240,
+# vocabulary 166144), rank-64 adapter, block 8. "small" and "small_looped": reduced
+# stacks of the same structure for oracle comparisons. Four sequences per step.
+STEP_CONFIGS = {
+    "qwen": dict(hidden=4096, kv_width=1024, head_dim=128, ffn=12288, vocab=151936, layers=36, rank=128,
+                 b=16, S=4, loops=1),
+    "looped": dict(hidden=2560, kv_width=2560, head_dim=128, ffn=10240, vocab=166144, layers=22, rank=64,
+                   b=8, S=4, loops=2),
+    "small": dict(hidden=1024, kv_width=256, head_dim=128, ffn=3072, vocab=32000, layers=2, rank=64,
+                  b=8, S=4, loops=1),
+    "small_looped": dict(hidden=768, kv_width=768, head_dim=128, ffn=2048, vocab=20000, layers=2, rank=32,
+                         b=8, S=4, loops=2),
+}
+STEP_PROJ_SHAPES = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+def step_proj_dims(cfg):
+    """(out, in) of the seven projections of one layer."""
+    H, KV, F = cfg["hidden"], cfg["kv_width"], cfg["ffn"]
+    return [(H, H), (KV, H), (KV, H), (H, H), (F, H), (F, H), (H, F)]
+
+
+def step_model_host(cfg, seed=0, embed_sigma=1.0, weight_sigma=0.02, lora_sigma=0.01):
+    """A decoder stack as bf16 bit patterns (uint16): embed / lm_head [V, H] ~
+    N(0, embed_sigma^2) / N(0, weight_sigma^2); projection weights [out, in] ~
+    N(0, weight_sigma^2); adapter factors A [r, in], B [out, r] ~ N(0, lora_sigma^2)."""
+    c = STEP_CONFIGS[cfg] if isinstance(cfg, str) else cfg
+    V, H, r = c["vocab"], c["hidden"], c["rank"]
+
+    def draw(sigma, shape, *key):
+        return to_bf16_bits(np.float32(sigma) * _rng(seed, 200, *key).standard_normal(shape, dtype=np.float32))
+
+    m = dict(embed=draw(embed_sigma, (V, H), 0), lm_head=draw(weight_sigma, (V, H), 1),
+             weights=[], lora_a=[], lora_b=[], head_dim=c["head_dim"], rank=r, lora_scale=1.0)
+    for layer in range(c["layers"]):
+        dims = step_proj_dims(c)
+        m["weights"].append([draw(weight_sigma, d, 2, layer, j) for j, d in enumerate(dims)])
+        if r:
+            m["lora_a"].append([draw(lora_sigma, (r, d[1]), 3, layer, j) for j, d in enumerate(dims)])
+            m["lora_b"].append([draw(lora_sigma, (d[0], r), 4, layer, j) for j, d in enumerate(dims)])
+    return m
+
+
+def step_model_torch(cfg, device, seed=0, embed_sigma=1.0, weight_sigma=0.02, lora_sigma=0.01):
+    """The same structure drawn on `device` by torch's generator (for the full-size
+    stacks, whose 10^10 weights are too many to draw on the host)."""
+    import torch
+    c = STEP_CONFIGS[cfg] if isinstance(cfg, str) else cfg
+    V, H, r = c["vocab"], c["hidden"], c["rank"]
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 7919 + 17)
+
+    def draw(sigma, shape):
+        return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * sigma).to(torch.bfloat16)
+
+    m = dict(embed=draw(embed_sigma, (V, H)), lm_head=draw(weight_sigma, (V, H)), weights=[], lora_a=[],
+             lora_b=[], head_dim=c["head_dim"], rank=r, lora_scale=1.0)
+    for _ in range(c["layers"]):
+        dims = step_proj_dims(c)
+        m["weights"].append([draw(weight_sigma, d) for d in dims])
+        if r:
+            m["lora_a"].append([draw(lora_sigma, (r, d[1])) for d in dims])
+            m["lora_b"].append([draw(lora_sigma, (d[0], r)) for d in dims])
+    return m
