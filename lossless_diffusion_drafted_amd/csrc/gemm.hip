@@ -379,6 +379,8 @@ struct SkinnyParams {
 
 constexpr int SK_COLS = 32;        // output columns per workgroup
 constexpr int SK_GROUP = 128;      // reduction elements per group
+constexpr int SK_MAX_SLICES = 8;   // K slices of one product at most
+constexpr int kBufDeviceCoherent = 16;   // SC1 cache policy: coherent across the device's L2s
 
 template <int MB>
 __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
@@ -451,12 +453,19 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
   };
   // Two register sets, so every index is a constant: the next group's loads are in
   // flight while the current group is multiplied.
+  // The scheduling barriers keep each group's loads ahead of the previous group's
+  // MFMAs; without them the compiler sank the loads below the MFMAs and waited for
+  // nearly all of them at the top of the loop, leaving one group in flight.
   load(g0, xa, wa);
   for (int g = g0; g < g1; g += 2) {
     load(g + 1, xb, wb);
+    __builtin_amdgcn_sched_barrier(0);
     mma(xa, wa);
+    __builtin_amdgcn_sched_barrier(0);
     load(g + 2, xa, wa);
+    __builtin_amdgcn_sched_barrier(0);
     if (g + 1 < g1) mma(xb, wb);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Delta segment: r more reduction steps, 32 wide, on the tile's last wave.
@@ -496,14 +505,18 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
       for (int v = 0; v < 4; ++v) red[wave][i * 16 + 4 * fg + v][j * 16 + fr] = acc[i][j][v];
   __syncthreads();
 
+  // the row mask of the epilogue, read once per row
+  __shared__ float rowscale[ROWS];
+  const int rows = p.M < ROWS ? p.M : ROWS;
+  if (tid < rows) rowscale[tid] = (p.mask && p.mask[tid] == 0) ? 0.0f : p.scale;
+  __syncthreads();
   auto store = [&](int m, int n, float s) {
-    const float y = (p.mask && p.mask[m] == 0) ? 0.0f : p.scale * s;
+    const float y = rowscale[m] * s;
     if (p.yf)
       p.yf[size_t(m) * p.N + n] = y;
     else
       p.y[size_t(m) * p.N + n] = __builtin_bit_cast(uint16_t, (__bf16)y);
   };
-  const int rows = p.M < ROWS ? p.M : ROWS;
   if (p.KS == 1) {
     for (int e = tid; e < rows * SK_COLS; e += 256) {
       const int m = e / SK_COLS, c = e % SK_COLS, n = n0 + c;
@@ -528,13 +541,33 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
   }
   __syncthreads();
   if (!s_last) return;
-  for (int e = tid; e < rows * SK_COLS; e += 256) {
-    const int m = e / SK_COLS, c = e % SK_COLS, n = n0 + c;
-    if (n >= p.N) continue;
-    float s = 0.0f;
-    for (int q = 0; q < p.KS; ++q)
-      s += __hip_atomic_load(&p.part[(size_t(q) * p.M + m) * p.N + n], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    store(m, n, s);
+  // The slice tiles are read with device-coherent loads (the SC1 policy, what an
+  // agent-scope atomic load uses), all of a batch's loads issued before the first
+  // is summed: one memory round trip per batch, not one per load.
+  const __amdgpu_buffer_rsrc_t rp = make_row_rsrc(p.part, uint32_t(size_t(p.KS) * p.M * p.N * 4));
+  constexpr int EB = 4;                                  // elements per thread per batch
+  for (int e0 = tid; e0 < rows * SK_COLS; e0 += 256 * EB) {
+    float v[EB][SK_MAX_SLICES];
+#pragma unroll
+    for (int u = 0; u < EB; ++u) {
+      const int e = e0 + u * 256, m = e / SK_COLS, n = n0 + e % SK_COLS;
+      const bool ok = e < rows * SK_COLS && n < p.N;
+#pragma unroll
+      for (int q = 0; q < SK_MAX_SLICES; ++q)
+        v[u][q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+            rp, (ok && q < p.KS) ? uint32_t(((size_t(q) * p.M + m) * p.N + n) * 4) : kOutOfRange, 0u,
+            kBufDeviceCoherent));
+    }
+#pragma unroll
+    for (int u = 0; u < EB; ++u) {
+      const int e = e0 + u * 256, m = e / SK_COLS, n = n0 + e % SK_COLS;
+      if (e >= rows * SK_COLS || n >= p.N) continue;
+      float s = 0.0f;
+#pragma unroll
+      for (int q = 0; q < SK_MAX_SLICES; ++q)
+        if (q < p.KS) s += v[u][q];
+      store(m, n, s);
+    }
   }
   if (tid == 0) __hip_atomic_store(&p.ticket[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -545,7 +578,8 @@ int skinny_slices(int N, int K) {
   const int tiles = (N + SK_COLS - 1) / SK_COLS;
   const int G = K / SK_GROUP;
   int ks = (256 + tiles - 1) / tiles;
-  const int cap = G / 4 > 1 ? G / 4 : 1;
+  int cap = G / 4 > 1 ? G / 4 : 1;
+  if (cap > SK_MAX_SLICES) cap = SK_MAX_SLICES;
   return ks < cap ? ks : cap;
 }
 
