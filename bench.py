@@ -51,6 +51,16 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
 COPY_BYTES = 1 << 30            # size of the calibration copy
 
+# Device functions launched by each timed entry point: the traffic summary counts
+# only these (a counter run also holds the setup's other kernels, such as the draft
+# sampler that makes the verifier's draft tokens).
+KERNEL_FUNCTIONS = {
+    "verify": ("verify_kernel",),
+    "gated_lora_attn_4096x4096": ("gemm_kernel", "lora_down_kernel", "skinny_kernel"),
+    "gated_lora_mlp_4096x12288": ("gemm_kernel", "lora_down_kernel", "skinny_kernel"),
+    "tv": ("tv_kernel", "tv_count_kernel"),
+}
+
 # Source file of each timed entry point (the traffic summary is tied to its hash).
 KERNEL_SOURCES = {
     "verify": "lossless_diffusion_drafted_amd/csrc/verify.hip",
@@ -274,6 +284,11 @@ def summarize_pmc(directory, name):
     (pmc_copy/copy_fetch, pmc_copy/copy_write), each a rocprofv3 --pmc CSV."""
     only = [k for k, v in ONLY.items() if v == name][0]
 
+    def function_of(kname):
+        # "void uno::(anonymous namespace)::verify_kernel<unsigned short, true>(uno::VerifyArgs)"
+        head = kname.split("(uno::")[0] if "(uno::" in kname else kname
+        return head.replace("void ", "").replace("uno::(anonymous namespace)::", "").replace("uno::", "")
+
     def per_call(sub, counter, copy):
         files = glob.glob(os.path.join(directory, sub, "**", "*counter_collection.csv"), recursive=True)
         if not files:
@@ -290,10 +305,12 @@ def summarize_pmc(directory, name):
                     if copy and "neg" not in kname:
                         continue
                     v = float(row["Counter_Value"])
+                    short = function_of(kname)
+                    kernels[short] = kernels.get(short, 0.0) + v
+                    if not copy and not any(short.startswith(fn) for fn in KERNEL_FUNCTIONS[name]):
+                        continue                # a setup kernel of the run, not the timed entry point
                     total += v
                     dispatches.add(row.get("Dispatch_Id"))
-                    short = kname.split("(")[0].replace("uno::(anonymous namespace)::", "")
-                    kernels[short] = kernels.get(short, 0.0) + v
         return total, len(dispatches), kernels
 
     calls = int(os.environ.get("PMC_CALLS", "0"))
@@ -322,9 +339,11 @@ def summarize_pmc(directory, name):
                     f"--warmup 1\n")
         f.write(f"    PMC_CALLS={calls} PMC_COPY_CALLS={copy_calls} python3 bench.py --summarize-pmc gpurun_out "
                 f"--kernel {name}\n\n")
-        f.write("Counters are summed over every dispatch of the library's kernels in the run and divided by\n"
-                "the number of calls. The KiB counts are scaled by the copy calibration: a plain\n"
-                f"elementwise copy (torch.neg) of {COPY_BYTES} B reads and writes exactly that many bytes.\n\n")
+        f.write("Counters are summed over the dispatches of the entry point's own kernels "
+                f"({', '.join(KERNEL_FUNCTIONS[name])}) and divided by\n"
+                "the number of calls; the run's setup kernels are listed below but not counted. The KiB\n"
+                "counts are scaled by the copy calibration: a plain elementwise copy (torch.neg) of\n"
+                f"{COPY_BYTES} B reads and writes exactly that many bytes.\n\n")
         f.write(f"- source: `{KERNEL_SOURCES[name]}`\n")
         f.write(f"- source_sha256: `{source_sha256(name)}`\n")
         f.write(f"- calls: {calls}\n")
@@ -337,7 +356,7 @@ def summarize_pmc(directory, name):
         f.write(f"- hbm_fetch_bytes_per_call: {fetch:.0f}\n")
         f.write(f"- hbm_write_bytes_per_call: {write:.0f}\n")
         f.write(f"- hbm_bytes_per_call: {fetch + write:.0f}\n\n")
-        f.write("Per-kernel FETCH_SIZE / WRITE_SIZE (KiB per call):\n\n")
+        f.write("Every kernel of the runs, FETCH_SIZE / WRITE_SIZE (KiB per timed call):\n\n")
         for k in sorted(set(f_k) | set(w_k)):
             f.write(f"    {k}: fetch {f_k.get(k, 0.0) / calls:.1f}  write {w_k.get(k, 0.0) / calls:.1f}\n")
     print(out)
