@@ -41,6 +41,14 @@ __device__ __forceinline__ uint4 load_nt16(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// s_waitcnt lgkmcnt(0) (LDS, scalar memory) with the other counters left alone.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
 // Raw buffer loads: a range-checked view of one row. Reads past num_records
 // return zero instead of faulting, so every lane issues exactly one load per chunk
 // and the compiler can count outstanding loads across a pipelined loop.
@@ -53,6 +61,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_row_rsrc(const void* base
 // and on gfx950 this raises sustained read bandwidth (measured 6.0 -> 6.9 TB/s
 // on a 600 MB row stream).
 constexpr int kBufNonTemporal = 2;
+// SC1 cache policy: the load is coherent across the device's L2s (what an
+// agent-scope atomic load uses).
+constexpr int kBufDeviceCoherent = 16;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kBufNonTemporal);
   return make_uint4(v.x, v.y, v.z, v.w);

@@ -30,7 +30,6 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past any range: reads 0
 
@@ -82,12 +81,6 @@ struct GemmParams {
   const uint8_t* mask1;    // row mask applied to segment 1's A rows (may be null)
   uint16_t* y;             // bf16 [M, N]
 };
-
-// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams p) {
@@ -380,7 +373,6 @@ struct SkinnyParams {
 constexpr int SK_COLS = 32;        // output columns per workgroup
 constexpr int SK_GROUP = 128;      // reduction elements per group
 constexpr int SK_MAX_SLICES = 8;   // K slices of one product at most
-constexpr int kBufDeviceCoherent = 16;   // SC1 cache policy: coherent across the device's L2s
 
 template <int MB>
 __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {

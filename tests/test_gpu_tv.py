@@ -77,7 +77,10 @@ def _check(gpu, ref_loss, ref_rows, ref_grad, mask, T=1.0):
         assert np.all(sums <= 2 ** -8 * np.abs(g).sum(axis=1) + 1e-6 / (T * n))
 
 
-# A row is split over a team of ceil(V / 40960) workgroups (1024 threads x 40 logits).
+# A row is split over a team of workgroups. bf16 rows with 16-byte alignment take
+# the pipelined kernel: ceil(V / 30720) members (960 data threads x 32 logits).
+# fp32 rows and unaligned rows take the register kernel: ceil(V / 40960) members
+# (1024 threads x 40 logits).
 @pytest.mark.parametrize("R,V,dtype,T,mask_kind", [
     (5, 1000, "bf16", 1.0, "all"),        # one workgroup per row, ragged slice
     (16, 1000, "bf16", 1.0, "random"),
@@ -85,11 +88,13 @@ def _check(gpu, ref_loss, ref_rows, ref_grad, mask, T=1.0):
     (13, 50000, "f32", 1.0, "random"),    # fp32 logits
     (9, 30001, "f32", 1.3, "all"),        # rows not 16-byte aligned
     (7, 4097, "bf16", 1.0, "random"),     # rows not 16-byte aligned
-    (6, 151936, "bf16", 1.0, "all"),      # the full vocabulary: four-member teams
-    (3, 163840, "bf16", 1.0, "all"),      # exactly fills four slices
-    (4, 262144, "bf16", 1.0, "all"),      # seven-member teams
+    (6, 151936, "bf16", 1.0, "all"),      # the full vocabulary: five-member teams
+    (3, 153600, "bf16", 1.0, "all"),      # exactly fills five slices
+    (4, 262144, "bf16", 1.0, "all"),      # nine-member teams
     (3, 1000000, "f32", 0.9, "random"),   # 25-member teams, fp32
-    (2, 64 * 40960 - 5, "bf16", 1.0, "all"),   # the largest team (64 members), ragged
+    (2, 64 * 30720 - 8, "bf16", 1.0, "all"),    # the largest team (64 members), ragged
+    (2, 64 * 30720 - 5, "bf16", 1.0, "all"),    # unaligned rows: 48-member teams
+    (2, 64 * 40960 - 4, "f32", 1.0, "all"),     # the largest fp32 team (64 members)
 ])
 def test_tv_matches_oracle(R, V, dtype, T, mask_kind):
     t, s = _inputs(R, V, dtype, seed=R * 7 + V)
@@ -115,7 +120,7 @@ def test_tv_forward_only_and_optional_rows():
 
 def test_tv_vocabulary_beyond_the_largest_team_is_rejected():
     uno = _uno()
-    V = 64 * 40960 + 1
+    V = 64 * 30720 + 8
     z = torch.zeros((1, V), dtype=torch.bfloat16, device=DEV)
     m = torch.ones((1,), dtype=torch.uint8, device=DEV)
     with pytest.raises(uno.UnoError) as e:
