@@ -4,6 +4,7 @@ Usage: python -m lossless_diffusion_drafted_amd.build [--verbose]
 """
 
 import concurrent.futures
+import ctypes
 import os
 import shutil
 import subprocess
@@ -55,6 +56,12 @@ def build(verbose=False):
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("link of libuno.so failed")
+    # a shared library links with unresolved symbols; loading it finds them now
+    # rather than in the first call
+    try:
+        ctypes.CDLL(tmp)
+    except OSError as e:
+        raise RuntimeError(f"libuno.so does not load: {e}")
     os.replace(tmp, LIB)
     if verbose:
         sys.stderr.write(f"built {LIB}\n")

@@ -564,6 +564,191 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
   if (tid == 0) __hip_atomic_store(&p.ticket[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------------------
+// Small-M path, streaming form, for wide products (an LM head) at 17-64 rows.
+// The product above keeps one 128-wide group of loads in flight per wave, and at
+// 64 rows each wave also streams its own copy of X through registers: from HBM
+// (weights no cache holds, as in a decode step) the LM head at 64 rows ran at
+// 2.6 TB/s. Here the four waves of a workgroup own four adjacent 32-column blocks
+// (128 columns) over the whole reduction and share X:
+// * X: each 128-wide group's X rows go to LDS once per workgroup, by buffer loads
+//   that write LDS, in the MFMA operand order (the load for row block i and
+//   32-wide step c writes 1 KB that lane l later reads as its own 16 bytes), so the
+//   fragment reads are conflict-free. PD stages.
+// * W: each wave loads its own 32 rows of the group into registers, a ring of PD
+//   groups (PD - 1 in flight while one is multiplied): 8 KB per wave per group,
+//   about 100 KB per CU in flight.
+// * One barrier per group: the wait for group g's loads (in order, so W and X),
+//   then the barrier, publishes the X stage and retires every wave's reads of the
+//   stage refilled next.
+// * Each workgroup covers the whole reduction of its columns (products with at
+//   least 256 column tiles), so no partials cross waves or workgroups.
+constexpr int SK2_COLS = 128;      // output columns per workgroup (32 per wave)
+
+template <int MB, int PD>
+__global__ __launch_bounds__(256) void skinny2_kernel(SkinnyParams p) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  constexpr int NB = 2;                                 // 16-column blocks per wave
+  constexpr int XL = MB * 4;                            // X load instructions per group (1 KB each)
+  constexpr int XW = XL / 4;                            // ... per wave
+  constexpr int LPG = XW + NB * 4;                      // loads per wave per group
+  constexpr int STAGE = XL * 1024;                      // bytes of one X stage
+  __shared__ __attribute__((aligned(1024))) char xs[PD * STAGE];
+  __shared__ float rowscale[MB * 16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * SK2_COLS + wave * 32;
+  const int g0 = 0, g1 = p.K / SK_GROUP;                // the whole reduction
+  const int fr = lane & 15, fg = lane >> 4;
+
+  const __amdgpu_buffer_rsrc_t rx = make_row_rsrc(p.x, uint32_t(size_t(p.M) * p.K * 2));
+  const __amdgpu_buffer_rsrc_t rw = make_row_rsrc(p.w, uint32_t(size_t(p.N) * p.K * 2));
+  // X load q = wave + 4 e (row block q / 4, step q % 4); lane l reads row
+  // 16 (q / 4) + l % 16 at k = 32 (q % 4) + 8 (l / 16).
+  uint32_t xo[XW];
+  bool xin[XW];
+#pragma unroll
+  for (int e = 0; e < XW; ++e) {
+    const int q = wave + 4 * e, m = (q >> 2) * 16 + fr;
+    xin[e] = m < p.M;
+    xo[e] = uint32_t((size_t(m) * p.K + (q & 3) * 32 + fg * 8) * 2);
+  }
+  uint32_t wo[NB];
+  bool win[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int n = n0 + j * 16 + fr;
+    win[j] = n < p.N;
+    wo[j] = uint32_t((size_t(n) * p.K + fg * 8) * 2);
+  }
+
+  f32x4_t acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  u32x4_t wr[PD][NB][4];
+  // Group g's loads into X stage st and W set st; past the slice they read out of
+  // range (zeros), so every step issues LPG loads and the waits are static.
+  auto issue = [&](int g, int st, u32x4_t (&wv)[NB][4]) {
+    const bool live = g < g1;
+    const uint32_t kb = uint32_t(g) * SK_GROUP * 2;
+#pragma unroll
+    for (int e = 0; e < XW; ++e) {
+      // The offset goes through a variable: written inline in the call, it kept the
+      // host compiler from emitting the kernel's launch stub.
+      const uint32_t off = (live && xin[e]) ? xo[e] + kb : kOutOfRange;
+      char* dst = xs + st * STAGE + (wave + 4 * e) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)dst, 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        wv[j][c] = __builtin_amdgcn_raw_buffer_load_b128(rw, (live && win[j]) ? wo[j] + kb + c * 64 : kOutOfRange,
+                                                         0u, kBufNonTemporal);
+  };
+  auto mma = [&](int st, const u32x4_t (&wv)[NB][4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const u32x4_t xf = *reinterpret_cast<const u32x4_t*>(xs + st * STAGE + (i * 4 + c) * 1024 + lane * 16);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xf),
+                                                              __builtin_bit_cast(bf16x8_t, wv[j][c]),
+                                                              acc[i][j], 0, 0, 0);
+      }
+  };
+
+#pragma unroll
+  for (int s = 0; s < PD - 1; ++s) issue(g0 + s, s, wr[s]);
+  // Unrolled by PD so that every stage and register set index is a constant.
+  for (int gb = g0; gb < g1; gb += PD) {
+#pragma unroll
+    for (int s = 0; s < PD; ++s) {
+      const int g = gb + s;
+      if (g >= g1) break;
+      wait_vmcnt<(PD - 2) * LPG>();                   // group g's X and W have landed
+      __builtin_amdgcn_s_barrier();                   // X stage of g complete; stage (g - 1) free
+      issue(g + PD - 1, (s + PD - 1) % PD, wr[(s + PD - 1) % PD]);
+      mma(s, wr[s]);
+    }
+  }
+  wait_vmcnt<0>();
+
+  // Delta segment [T | B]: r more reduction steps, 32 wide.
+  if (p.r > 0) {
+    const __amdgpu_buffer_rsrc_t rt = make_row_rsrc(p.t, uint32_t(size_t(p.M) * p.r * 2));
+    const __amdgpu_buffer_rsrc_t rb = make_row_rsrc(p.b, uint32_t(size_t(p.N) * p.r * 2));
+    for (int s0 = 0; s0 < p.r; s0 += 32) {
+      u32x4_t tv[MB], bv[NB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int m = i * 16 + fr;
+        tv[i] = __builtin_amdgcn_raw_buffer_load_b128(
+            rt, m < p.M ? uint32_t((size_t(m) * p.r + s0 + fg * 8) * 2) : kOutOfRange, 0u, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int n = n0 + j * 16 + fr;
+        bv[j] = __builtin_amdgcn_raw_buffer_load_b128(
+            rb, n < p.N ? uint32_t((size_t(n) * p.r + s0 + fg * 8) * 2) : kOutOfRange, 0u, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tv[i]),
+                                                              __builtin_bit_cast(bf16x8_t, bv[j]),
+                                                              acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // the row mask of the epilogue, read once per row
+  const int rows = p.M < MB * 16 ? p.M : MB * 16;
+  if (tid < rows) rowscale[tid] = (p.mask && p.mask[tid] == 0) ? 0.0f : p.scale;
+  __syncthreads();
+  auto store = [&](int m, int n, float v) {
+    const float y = rowscale[m] * v;
+    if (p.yf)
+      p.yf[size_t(m) * p.N + n] = y;
+    else
+      p.y[size_t(m) * p.N + n] = __builtin_bit_cast(uint16_t, (__bf16)y);
+  };
+  // Accumulator v of lane l of a 16 x 16 block is row 4 (l / 16) + v, column l % 16.
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = i * 16 + 4 * fg + v, n = n0 + j * 16 + fr;
+        if (m < p.M && n < p.N) store(m, n, acc[i][j][v]);
+      }
+}
+
+
+// Which small-M form a product takes. Measured from HBM (each call a different
+// weight), the streaming form won only where its workgroups each cover the whole
+// reduction (products with at least 256 column tiles of 128, such as an LM
+// head) and M > 16: the LM head 4096 -> 151936 at 64 rows took 366 against
+// 483 us. Elsewhere its short slices and the last slice's sum over 128-column
+// partial tiles cost more than they save (q 4096 -> 4096 at 64 rows: 22.6 against
+// 19.9 us), and at M <= 16 it was slower throughout (LM head at 4 rows: 290
+// against 259 us).
+bool use_skinny2(int M, int N, int K) { return M > 16 && (N + SK2_COLS - 1) / SK2_COLS >= 256; }
+
+void launch_skinny2(const SkinnyParams& p, hipStream_t stream) {
+  const dim3 grid((p.N + SK2_COLS - 1) / SK2_COLS);
+  if (p.M <= 32)
+    skinny2_kernel<2, 4><<<grid, dim3(256), 0, stream>>>(p);
+  else
+    skinny2_kernel<4, 4><<<grid, dim3(256), 0, stream>>>(p);
+}
+
 // K slices of a small-M product: about one workgroup per CU (measured best
 // against 2, 4 and 8 per CU), each wave at least one 128-wide group.
 int skinny_slices(int N, int K) {
@@ -694,8 +879,17 @@ void launch_main(const GemmParams& g, hipStream_t stream) {
 constexpr size_t kTicketBytes = 65536;
 constexpr int kMaxTickets = int(kTicketBytes / 4);
 
+int small_slices(int M, int N, int K) { return use_skinny2(M, N, K) ? 1 : skinny_slices(N, K); }
+
+void launch_small(const SkinnyParams& p, hipStream_t stream) {
+  if (use_skinny2(p.M, p.N, p.K))
+    launch_skinny2(p, stream);
+  else
+    launch_skinny(p, stream);
+}
+
 size_t skinny_part_bytes(int M, int N, int K, int r) {
-  int ks = skinny_slices(N, K), ks_r = r > 0 ? skinny_slices(r, K) : 1;
+  int ks = small_slices(M, N, K), ks_r = r > 0 ? small_slices(M, r, K) : 1;
   size_t big = 0;
   if (ks > 1) big = size_t(ks) * M * N * 4;
   if (ks_r > 1 && size_t(ks_r) * M * r * 4 > big) big = size_t(ks_r) * M * r * 4;
@@ -736,23 +930,23 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
       p.w = static_cast<const uint16_t*>(a.A);
       p.N = a.r;
       p.r = 0;
-      p.KS = skinny_slices(a.r, a.K);
+      p.KS = small_slices(a.M, a.r, a.K);
       p.scale = a.scale;
       p.mask = a.row_mask;
       p.y = tws;
-      launch_skinny(p, stream);
+      launch_small(p, stream);
     }
     p.w = static_cast<const uint16_t*>(a.W);
     p.N = a.N;
     p.r = a.r;
     p.t = a.r > 0 ? tws : nullptr;
     p.b = static_cast<const uint16_t*>(a.B);
-    p.KS = skinny_slices(a.N, a.K);
+    p.KS = small_slices(a.M, a.N, a.K);
     p.scale = 1.0f;
     p.mask = nullptr;
     p.y = a.y_f32 ? nullptr : static_cast<uint16_t*>(a.Y);
     p.yf = a.y_f32 ? static_cast<float*>(a.Y) : nullptr;
-    launch_skinny(p, stream);
+    launch_small(p, stream);
     return hipGetLastError();
   }
   const uint16_t* tmat = nullptr;

@@ -106,6 +106,9 @@ def test_ragged_shapes(M, K, N, r):
     (64, 12288, 4096, 128),
     (64, 4096, 151936, 0),     # the LM head at a step's rows
     (48, 256, 72, 96),         # reduction shorter than one slice of four waves
+    # wide products at 17-64 rows take the streaming form (128 columns per workgroup)
+    (24, 512, 32768 + 40, 32),    # ragged columns, a delta segment, 32-row blocks
+    (40, 256, 33000, 64),         # ragged rows and columns, 64-row blocks
 ])
 def test_small_m_shapes(M, K, N, r):
     """Row counts of a decode step (M <= 64) take the weight-streaming path."""
