@@ -22,6 +22,8 @@
 // is staged through LDS and written with 16-byte stores.
 
 #include "../../include/uno.h"
+
+#include <climits>
 #include "common.h"
 #include "kernels.h"
 
@@ -359,9 +361,13 @@ __global__ __launch_bounds__(LD_WAVES * 64) void lora_down_kernel(const uint16_t
 struct SkinnyParams {
   const uint16_t* x;      // [M, K]
   const uint16_t* w;      // [N, K]
-  const uint16_t* t;      // [M, r] delta rows (scaled and gated), or null when r == 0
+  const uint16_t* t;      // [M, t_stride] delta rows (scaled and gated), or null when r == 0
   const uint16_t* b;      // [N, r]
   int M, N, K, r, KS;
+  // Grouped products: T holds the groups' delta rows side by side (row stride
+  // t_stride); columns from nb1 on use T's second block of r, from nb2 on its
+  // third (INT_MAX: one group).
+  int t_stride, nb1, nb2;
   float scale;            // epilogue: y = mask[m] ? scale * acc : 0 (mask may be null)
   const uint8_t* mask;
   uint16_t* y;            // [M, N] bf16
@@ -462,15 +468,16 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
 
   // Delta segment: r more reduction steps, 32 wide, on the tile's last wave.
   if (p.r > 0 && wi == nw - 1) {
-    const __amdgpu_buffer_rsrc_t rt = make_row_rsrc(p.t, uint32_t(size_t(p.M) * p.r * 2));
+    const __amdgpu_buffer_rsrc_t rt = make_row_rsrc(p.t, uint32_t(size_t(p.M) * p.t_stride * 2));
     const __amdgpu_buffer_rsrc_t rb = make_row_rsrc(p.b, uint32_t(size_t(p.N) * p.r * 2));
+    const int toff = ((n0 >= p.nb1) + (n0 >= p.nb2)) * p.r;   // this tile's group block of T
     for (int s0 = 0; s0 < p.r; s0 += 32) {
       u32x4_t tv[MB], bv[NB];
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
         const int m = i * 16 + fr;
         tv[i] = __builtin_amdgcn_raw_buffer_load_b128(
-            rt, m < p.M ? uint32_t((size_t(m) * p.r + s0 + fg * 8) * 2) : kOutOfRange, 0u, 0);
+            rt, m < p.M ? uint32_t((size_t(m) * p.t_stride + toff + s0 + fg * 8) * 2) : kOutOfRange, 0u, 0);
       }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
@@ -681,15 +688,16 @@ __global__ __launch_bounds__(256) void skinny2_kernel(SkinnyParams p) {
 
   // Delta segment [T | B]: r more reduction steps, 32 wide.
   if (p.r > 0) {
-    const __amdgpu_buffer_rsrc_t rt = make_row_rsrc(p.t, uint32_t(size_t(p.M) * p.r * 2));
+    const __amdgpu_buffer_rsrc_t rt = make_row_rsrc(p.t, uint32_t(size_t(p.M) * p.t_stride * 2));
     const __amdgpu_buffer_rsrc_t rb = make_row_rsrc(p.b, uint32_t(size_t(p.N) * p.r * 2));
+    const int toff = ((n0 >= p.nb1) + (n0 >= p.nb2)) * p.r;   // this wave's group block of T
     for (int s0 = 0; s0 < p.r; s0 += 32) {
       u32x4_t tv[MB], bv[NB];
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
         const int m = i * 16 + fr;
         tv[i] = __builtin_amdgcn_raw_buffer_load_b128(
-            rt, m < p.M ? uint32_t((size_t(m) * p.r + s0 + fg * 8) * 2) : kOutOfRange, 0u, 0);
+            rt, m < p.M ? uint32_t((size_t(m) * p.t_stride + toff + s0 + fg * 8) * 2) : kOutOfRange, 0u, 0);
       }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
@@ -914,10 +922,12 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     ws += kTicketBytes;
   }
   uint16_t* tws = reinterpret_cast<uint16_t*>(ws);
-  float* part = reinterpret_cast<float*>(ws + (a.r > 0 ? align256(size_t(a.M) * a.r * 2) : 0));
+  const int rt = a.r * a.groups;                  // columns of T
+  float* part = reinterpret_cast<float*>(ws + (a.r > 0 ? align256(size_t(a.M) * rt * 2) : 0));
   const bool small = skinny_ok(a.M, a.N, a.K, a.r, a.X, a.W, a.A, a.B) &&
-                     (a.N + SK_COLS - 1) / SK_COLS <= kMaxTickets && (a.r + SK_COLS - 1) / SK_COLS <= kMaxTickets;
+                     (a.N + SK_COLS - 1) / SK_COLS <= kMaxTickets && (rt + SK_COLS - 1) / SK_COLS <= kMaxTickets;
   if (a.y_f32 && !small) return hipErrorInvalidValue;   // fp32 output exists on the small-M path only
+  if (a.groups < 1 || a.groups > 3 || (a.groups > 1 && !small)) return hipErrorInvalidValue;
   if (small) {
     SkinnyParams p{};
     p.M = a.M;
@@ -925,12 +935,16 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     p.part = part;
     p.ticket = tickets;
     p.x = static_cast<const uint16_t*>(a.X);
+    p.t_stride = rt;
+    p.nb1 = a.groups > 1 ? a.gstart[0] : INT_MAX;
+    p.nb2 = a.groups > 2 ? a.gstart[1] : INT_MAX;
     if (a.r > 0) {
-      // T = bf16(s * diag(mask) X A^T): the same product with A in place of W
+      // T = bf16(s * diag(mask) X A^T): the same product with A in place of W (the
+      // groups' A blocks stacked: T holds their delta rows side by side)
       p.w = static_cast<const uint16_t*>(a.A);
-      p.N = a.r;
+      p.N = rt;
       p.r = 0;
-      p.KS = small_slices(a.M, a.r, a.K);
+      p.KS = small_slices(a.M, rt, a.K);
       p.scale = a.scale;
       p.mask = a.row_mask;
       p.y = tws;

@@ -67,6 +67,12 @@ struct GemmArgs {
   void* ws;
   unsigned* tickets = nullptr;   // slice tickets kept apart from ws (else the first 64 KB of ws)
   bool y_f32 = false;            // Y is fp32 (small-M path only)
+  // Grouped products (small-M path only): W, A and B stack `groups` products that
+  // share X; group g owns columns [gstart[g-1], gstart[g]) of Y and rows
+  // [g r, (g + 1) r) of A, and B stacks the groups' B rows like W. gstart values
+  // are multiples of 32. The workspace is sized for rank groups * r.
+  int groups = 1;
+  int gstart[2] = {0, 0};
 };
 
 size_t verify_workspace_bytes(int S, int b);

@@ -100,9 +100,10 @@ __global__ __launch_bounds__(MT) void norm_kernel(const int32_t* tokens, const u
 }
 
 // a[m, j] = v[m, kv_head(j) * hd + j % hd]: attention over a one-token context
-// returns each query head its kv head's value row. 16-byte copies (hd % 8 == 0).
-__global__ __launch_bounds__(MT) void expand_kernel(const uint16_t* v, uint16_t* a, int M, int H, int KVW,
-                                                    int hd) {
+// returns each query head its kv head's value row (v rows vstride apart).
+// 16-byte copies (hd % 8 == 0).
+__global__ __launch_bounds__(MT) void expand_kernel(const uint16_t* v, int vstride, uint16_t* a, int M, int H,
+                                                    int KVW, int hd) {
   const int nc = H / 8;
   const int group = (H / hd) / (KVW / hd);
   for (size_t e = size_t(blockIdx.x) * MT + threadIdx.x; e < size_t(M) * nc; e += size_t(gridDim.x) * MT) {
@@ -110,20 +111,23 @@ __global__ __launch_bounds__(MT) void expand_kernel(const uint16_t* v, uint16_t*
     const int j = c * 8, head = j / hd;
     const int src = (head / group) * hd + j % hd;
     *reinterpret_cast<uint4*>(a + size_t(m) * H + j) =
-        *reinterpret_cast<const uint4*>(v + size_t(m) * KVW + src);
+        *reinterpret_cast<const uint4*>(v + size_t(m) * vstride + src);
   }
 }
 
-// out = bf16(silu(g) * u), silu(g) = g / (1 + exp(-g)), in fp32.
-__global__ __launch_bounds__(MT) void silu_mul_kernel(const uint16_t* g, const uint16_t* u, uint16_t* out,
-                                                      size_t n8) {
-  for (size_t c = size_t(blockIdx.x) * MT + threadIdx.x; c < n8; c += size_t(gridDim.x) * MT) {
+// out[m, :] = bf16(silu(g[m, :]) * u[m, :]) over F columns, silu(g) = g / (1 +
+// exp(-g)) in fp32; g and u rows ld elements apart.
+__global__ __launch_bounds__(MT) void silu_mul_kernel(const uint16_t* g, const uint16_t* u, int ld, uint16_t* out,
+                                                      int M, int F) {
+  const int nc = F / 8;
+  for (size_t c = size_t(blockIdx.x) * MT + threadIdx.x; c < size_t(M) * nc; c += size_t(gridDim.x) * MT) {
+    const size_t m = c / nc, j = (c % nc) * 8;
     float gf[8], uf[8], o[8];
-    unpack8(*reinterpret_cast<const uint4*>(g + c * 8), gf);
-    unpack8(*reinterpret_cast<const uint4*>(u + c * 8), uf);
+    unpack8(*reinterpret_cast<const uint4*>(g + m * ld + j), gf);
+    unpack8(*reinterpret_cast<const uint4*>(u + m * ld + j), uf);
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = gf[e] / (1.0f + expf(-gf[e])) * uf[e];
-    *reinterpret_cast<uint4*>(out + c * 8) = pack8(o);
+    *reinterpret_cast<uint4*>(out + m * F + j) = pack8(o);
   }
 }
 
@@ -161,16 +165,20 @@ constexpr size_t kStepHead = kStepTickets + kStepVerify;
 
 struct FwdBufs {
   uint16_t *h, *x, *q, *k, *v, *a, *o, *g, *u, *mm, *d;
-  void* gemm;       // T and slice tiles of the gated products
+  uint16_t *qkv, *gu;   // outputs of the grouped q | k | v and gate | up products
+  void* gemm;           // T and slice tiles of the gated products
 };
 
 size_t gemm_scratch(const ModelDesc& md, int M) {
   const int H = md.hidden, F = md.ffn, KVW = md.kv_width;
-  const int shapes[8][2] = {{H, H}, {H, KVW}, {H, KVW}, {H, H}, {H, F}, {H, F}, {F, H}, {H, md.vocab}};
+  // {K, N, rank}: the seven projections, the grouped q | k | v and gate | up
+  // products (stacked ranks), the LM head
+  const int shapes[10][3] = {{H, H, 1},     {H, KVW, 1},       {H, KVW, 1}, {H, H, 1},
+                             {H, F, 1},     {H, F, 1},         {F, H, 1},   {H, H + 2 * KVW, 3},
+                             {H, 2 * F, 2}, {H, md.vocab, 0}};
   size_t n = 0;
-  for (int i = 0; i < 8; ++i) {
-    const int r = i < 7 ? md.rank : 0;
-    const size_t b = gemm_workspace_bytes(M, shapes[i][1], shapes[i][0], r);
+  for (int i = 0; i < 10; ++i) {
+    const size_t b = gemm_workspace_bytes(M, shapes[i][1], shapes[i][0], md.rank * shapes[i][2]);
     if (b > n) n = b;
   }
   return n;                 // includes the 64 KB ticket area, which the step keeps apart
@@ -195,17 +203,23 @@ FwdBufs carve(const ModelDesc& md, int M, char* p) {
   f.u = take(m * F);
   f.mm = take(m * F);
   f.d = take(m * H);
+  f.qkv = take(m * (H + 2 * KVW));
+  f.gu = take(m * 2 * F);
   f.gemm = p;
   return f;
 }
 
 size_t fwd_bytes(const ModelDesc& md, int M) {
   const size_t H = md.hidden, F = md.ffn, KVW = md.kv_width, m = M;
-  return al256(m * H * 2) * 6 + al256(m * KVW * 2) * 2 + al256(m * F * 2) * 3 + gemm_scratch(md, M);
+  return al256(m * H * 2) * 6 + al256(m * KVW * 2) * 2 + al256(m * F * 2) * 3 + al256(m * (H + 2 * KVW) * 2) +
+         al256(m * 2 * F * 2) + gemm_scratch(md, M);
 }
 
-hipError_t gated(const ModelDesc& md, int layer, int proj, const uint16_t* x, uint16_t* y, int M, int K, int N,
-                 const uint8_t* mask, unsigned* tickets, void* scratch, hipStream_t st) {
+// Projection `proj` of a layer, or with n > 1 the n projections proj .. proj + n -
+// 1 as one grouped product (their weights, and adapter factors, stacked in memory;
+// `cols` gives each one's output width).
+hipError_t gated(const ModelDesc& md, int layer, int proj, const uint16_t* x, uint16_t* y, int M, int K,
+                 const int* cols, int n, const uint8_t* mask, unsigned* tickets, void* scratch, hipStream_t st) {
   GemmArgs g{};
   g.X = x;
   g.W = md.w[layer * 7 + proj];
@@ -217,11 +231,35 @@ hipError_t gated(const ModelDesc& md, int layer, int proj, const uint16_t* x, ui
   g.scale = md.lora_scale;
   g.Y = y;
   g.M = M;
-  g.N = N;
   g.K = K;
+  g.N = 0;
+  for (int i = 0; i < n; ++i) {
+    if (i > 0) g.gstart[i - 1] = g.N;
+    g.N += cols[i];
+  }
+  g.groups = n;
   g.ws = scratch;
   g.tickets = tickets;
   return launch_gemm(g, st);
+}
+
+// Whether projections proj .. proj + n - 1 of a layer can run as one grouped
+// product: each one's weight (and adapter factors) directly after the previous
+// one's in memory, and every output width a multiple of 32.
+bool stacked(const ModelDesc& md, int layer, int proj, const int* cols, int n, int K, bool lora) {
+  auto next_to = [](const void* a, const void* b, size_t bytes) {
+    return static_cast<const char*>(a) + bytes == static_cast<const char*>(b);
+  };
+  for (int i = 0; i < n; ++i)
+    if (cols[i] % 32 != 0) return false;
+  for (int i = 1; i < n; ++i) {
+    const int j = layer * 7 + proj + i;
+    if (!next_to(md.w[j - 1], md.w[j], size_t(cols[i - 1]) * K * 2)) return false;
+    if (lora && (!next_to(md.lora_a[j - 1], md.lora_a[j], size_t(md.rank) * K * 2) ||
+                 !next_to(md.lora_b[j - 1], md.lora_b[j], size_t(cols[i - 1]) * md.rank * 2)))
+      return false;
+  }
+  return true;
 }
 
 // The forward of M rows through the stack (`loops` times) and the LM head.
@@ -234,20 +272,39 @@ hipError_t forward(const ModelDesc& md, const int32_t* tokens, const uint8_t* ma
   hipError_t e = hipGetLastError();
   const int eg = int((size_t(M) * H / 8 + MT - 1) / MT);
   const int fg = int((size_t(M) * F / 8 + MT - 1) / MT);
+  const bool lora = md.rank > 0 && mask != nullptr;
+  const int qkv_cols[3] = {H, KVW, KVW}, gu_cols[2] = {F, F}, hcol[1] = {H}, kcol[1] = {KVW}, fcol[1] = {F};
   for (int it = 0; it < loops && e == hipSuccess; ++it) {
     for (int l = 0; l < md.layers && e == hipSuccess; ++l) {
-      if ((e = gated(md, l, 0, f.x, f.q, M, H, H, mask, tickets, f.gemm, st)) != hipSuccess) break;
-      if ((e = gated(md, l, 1, f.x, f.k, M, H, KVW, mask, tickets, f.gemm, st)) != hipSuccess) break;
-      if ((e = gated(md, l, 2, f.x, f.v, M, H, KVW, mask, tickets, f.gemm, st)) != hipSuccess) break;
-      hipLaunchKernelGGL(expand_kernel, dim3(eg < 4096 ? eg : 4096), dim3(MT), 0, st, f.v, f.a, M, H, KVW,
+      // q | k | v and gate | up run as grouped products when stacked in memory: one
+      // launch (and one LoRA-down) instead of three or two, each short launch's
+      // fixed cost paid once.
+      const uint16_t* v = f.v;
+      int vstride = KVW;
+      if (stacked(md, l, 0, qkv_cols, 3, H, lora)) {
+        if ((e = gated(md, l, 0, f.x, f.qkv, M, H, qkv_cols, 3, mask, tickets, f.gemm, st)) != hipSuccess) break;
+        v = f.qkv + H + KVW;
+        vstride = H + 2 * KVW;
+      } else {
+        if ((e = gated(md, l, 0, f.x, f.q, M, H, hcol, 1, mask, tickets, f.gemm, st)) != hipSuccess) break;
+        if ((e = gated(md, l, 1, f.x, f.k, M, H, kcol, 1, mask, tickets, f.gemm, st)) != hipSuccess) break;
+        if ((e = gated(md, l, 2, f.x, f.v, M, H, kcol, 1, mask, tickets, f.gemm, st)) != hipSuccess) break;
+      }
+      hipLaunchKernelGGL(expand_kernel, dim3(eg < 4096 ? eg : 4096), dim3(MT), 0, st, v, vstride, f.a, M, H, KVW,
                          md.head_dim);
-      if ((e = gated(md, l, 3, f.a, f.o, M, H, H, mask, tickets, f.gemm, st)) != hipSuccess) break;
+      if ((e = gated(md, l, 3, f.a, f.o, M, H, hcol, 1, mask, tickets, f.gemm, st)) != hipSuccess) break;
       hipLaunchKernelGGL(norm_kernel, dim3(M), dim3(MT), 0, st, nullptr, nullptr, 0, f.h, f.o, f.x, H);
-      if ((e = gated(md, l, 4, f.x, f.g, M, H, F, mask, tickets, f.gemm, st)) != hipSuccess) break;
-      if ((e = gated(md, l, 5, f.x, f.u, M, H, F, mask, tickets, f.gemm, st)) != hipSuccess) break;
-      hipLaunchKernelGGL(silu_mul_kernel, dim3(fg < 4096 ? fg : 4096), dim3(MT), 0, st, f.g, f.u, f.mm,
-                         size_t(M) * F / 8);
-      if ((e = gated(md, l, 6, f.mm, f.d, M, F, H, mask, tickets, f.gemm, st)) != hipSuccess) break;
+      if (stacked(md, l, 4, gu_cols, 2, H, lora)) {
+        if ((e = gated(md, l, 4, f.x, f.gu, M, H, gu_cols, 2, mask, tickets, f.gemm, st)) != hipSuccess) break;
+        hipLaunchKernelGGL(silu_mul_kernel, dim3(fg < 4096 ? fg : 4096), dim3(MT), 0, st, f.gu, f.gu + F, 2 * F,
+                           f.mm, M, F);
+      } else {
+        if ((e = gated(md, l, 4, f.x, f.g, M, H, fcol, 1, mask, tickets, f.gemm, st)) != hipSuccess) break;
+        if ((e = gated(md, l, 5, f.x, f.u, M, H, fcol, 1, mask, tickets, f.gemm, st)) != hipSuccess) break;
+        hipLaunchKernelGGL(silu_mul_kernel, dim3(fg < 4096 ? fg : 4096), dim3(MT), 0, st, f.g, f.u, F, f.mm, M,
+                           F);
+      }
+      if ((e = gated(md, l, 6, f.mm, f.d, M, F, hcol, 1, mask, tickets, f.gemm, st)) != hipSuccess) break;
       hipLaunchKernelGGL(norm_kernel, dim3(M), dim3(MT), 0, st, nullptr, nullptr, 0, f.h, f.d, f.x, H);
       e = hipGetLastError();
     }

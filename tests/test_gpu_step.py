@@ -55,12 +55,23 @@ def _models(name):
     return _MODELS[name]
 
 
-def _device_model(host, c):
+def _device_model(host, c, stacked=True):
+    """The host stack on the device. stacked: each layer's q, k, v (and gate, up)
+    weights and adapter factors back to back in one allocation, as the benchmark's
+    stacks hold them, so the forward runs them as grouped products."""
     uno = _uno()
     dev = lambda a: to_device(a, DEV)
-    lora_a = [[dev(t) for t in layer] for layer in host["lora_a"]] if host["rank"] else None
-    lora_b = [[dev(t) for t in layer] for layer in host["lora_b"]] if host["rank"] else None
-    return uno.Model(dev(host["embed"]), dev(host["lm_head"]), [[dev(t) for t in layer] for layer in host["weights"]],
+
+    def layer_on_device(layer):
+        if not stacked:
+            return [dev(t) for t in layer]
+
+        def pack(ts):
+            return list(torch.split(dev(np.concatenate(ts, axis=0)), [t.shape[0] for t in ts], dim=0))
+        return pack(layer[0:3]) + [dev(layer[3])] + pack(layer[4:6]) + [dev(layer[6])]
+    lora_a = [layer_on_device(t) for t in host["lora_a"]] if host["rank"] else None
+    lora_b = [layer_on_device(t) for t in host["lora_b"]] if host["rank"] else None
+    return uno.Model(dev(host["embed"]), dev(host["lm_head"]), [layer_on_device(t) for t in host["weights"]],
                      lora_a, lora_b, kv_width=c["kv_width"], head_dim=c["head_dim"], lora_scale=host["lora_scale"])
 
 
@@ -72,10 +83,15 @@ def _inputs(S, V, seed):
     return seed_tok, seq, pos
 
 
-@pytest.mark.parametrize("name,loops", [("small", 1), ("small_looped", 2)])
-def test_forward_matches_oracle(name, loops):
+@pytest.mark.parametrize("name,loops,stacked", [("small", 1, True), ("small_looped", 2, True),
+                                                ("small", 1, False)])
+def test_forward_matches_oracle(name, loops, stacked):
+    """Logits of the forward against the oracle's, with the grouped q | k | v and
+    gate | up products (stacked weights) and without them."""
     uno = _uno()
     host, model = _models(name)
+    if not stacked:
+        model = _device_model(host, workloads.STEP_CONFIGS[name], stacked=False)
     V = host["embed"].shape[0]
     rng = np.random.default_rng(5)
     M = 40

@@ -257,10 +257,20 @@ def step_model_torch(cfg, device, seed=0, embed_sigma=1.0, weight_sigma=0.02, lo
 
     m = dict(embed=draw(embed_sigma, (V, H)), lm_head=draw(weight_sigma, (V, H)), weights=[], lora_a=[],
              lora_b=[], head_dim=c["head_dim"], rank=r, lora_scale=1.0)
+
+    def stacked(sigma, shapes):
+        # q, k, v (and gate, up) drawn as one allocation and split into row views, so
+        # that the forward can run them as one grouped product
+        rows = [s[0] for s in shapes]
+        return list(torch.split(draw(sigma, (sum(rows), shapes[0][1])), rows, dim=0))
+
+    def layer(sigma, shapes):
+        return stacked(sigma, shapes[0:3]) + [draw(sigma, shapes[3])] + stacked(sigma, shapes[4:6]) + \
+            [draw(sigma, shapes[6])]
     for _ in range(c["layers"]):
         dims = step_proj_dims(c)
-        m["weights"].append([draw(weight_sigma, d) for d in dims])
+        m["weights"].append(layer(weight_sigma, dims))
         if r:
-            m["lora_a"].append([draw(lora_sigma, (r, d[1])) for d in dims])
-            m["lora_b"].append([draw(lora_sigma, (d[0], r)) for d in dims])
+            m["lora_a"].append(layer(lora_sigma, [(r, d[1]) for d in dims]))
+            m["lora_b"].append(layer(lora_sigma, [(d[0], r) for d in dims]))
     return m
