@@ -84,13 +84,25 @@ struct GemmParams {
   uint16_t* y;             // bf16 [M, N]
 };
 
+// One product on a 2-D grid (tiles_a == 0), or two independent products sharing
+// one launch on a 1-D grid: workgroups [0, tiles_a) take pa's tiles, the rest pb's
+// (small products that would each leave most CUs idle).
 template <class C>
-__global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmParams pb, int tiles_a) {
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
-  const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
+  const bool second = tiles_a > 0 && int(blockIdx.x) >= tiles_a;
+  const GemmParams& p = second ? pb : pa;
+  int tile_m = blockIdx.y, tile_n = blockIdx.x;
+  if (tiles_a > 0) {
+    const int local = second ? int(blockIdx.x) - tiles_a : int(blockIdx.x);
+    const int ntx = (p.N + C::BN - 1) / C::BN;
+    tile_m = local / ntx;
+    tile_n = local % ntx;
+  }
+  const int m0 = tile_m * C::BM, n0 = tile_n * C::BN;
   const int k0len = p.seg[0].k, k1len = p.nseg > 1 ? p.seg[1].k : 0;
   const int n0tiles = (k0len + C::BK - 1) / C::BK;
   const int ntiles = n0tiles + (k1len + C::BK - 1) / C::BK;
@@ -258,17 +270,42 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams p) {
 // summed in LDS in wave order, scaled and rounded.
 constexpr int LD_WAVES = 8, LD_KC = 64, LD_PITCH = LD_KC + 8;   // pitch: bf16 per LDS row
 
-__global__ __launch_bounds__(LD_WAVES * 64) void lora_down_kernel(const uint16_t* X, const uint16_t* A, int M,
-                                                                  int K, int r, float scale, uint16_t* T,
-                                                                  const uint8_t* row_mask) {
+// One LoRA-down product of a launch (a launch may carry two: the backward's T and U).
+// Tt, when given, also receives the transposed tile, bf16(tscale * T) [r, M].
+struct LdJob {
+  const uint16_t* X;
+  const uint16_t* A;
+  int M, K, r;
+  float scale;
+  uint16_t* T;
+  const uint8_t* row_mask;
+  uint16_t* Tt;
+  float tscale;
+  int tiles;
+};
+struct LdJobs {
+  LdJob j[2];
+  int n;
+};
+
+__global__ __launch_bounds__(LD_WAVES * 64) void lora_down_kernel(LdJobs jobs) {
   constexpr int TILE = 32 * LD_PITCH;                 // bf16 per operand tile
   constexpr int STAGE_BYTES = LD_WAVES * 2 * TILE * 2;
   constexpr int RED_BYTES = LD_WAVES * 16 * 64 * 4;
   __shared__ __attribute__((aligned(16))) char smem[STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES];
   // Tiles of the same 32 X rows go to consecutive ids on one XCD (workgroups
   // are dealt to the 8 XCDs round robin), so each XCD's L2 fetches those rows once.
+  int tid_x = xcd_contiguous_id(int(blockIdx.x), int(gridDim.x));
+  const int jb = (jobs.n > 1 && tid_x >= jobs.j[0].tiles) ? 1 : 0;
+  const LdJob& jo = jobs.j[jb];
+  if (jb) tid_x -= jobs.j[0].tiles;
+  const uint16_t* X = jo.X;
+  const uint16_t* A = jo.A;
+  const int M = jo.M, K = jo.K, r = jo.r;
+  const float scale = jo.scale;
+  uint16_t* T = jo.T;
+  const uint8_t* row_mask = jo.row_mask;
   const int ttc = (r + 31) / 32;
-  const int tid_x = xcd_contiguous_id(int(blockIdx.x), int(gridDim.x));
   const int tm = tid_x / ttc, tc = tid_x % ttc;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem) + wave * 2 * TILE;
@@ -332,7 +369,12 @@ __global__ __launch_bounds__(LD_WAVES * 64) void lora_down_kernel(const uint16_t
     const int row = tm * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3), col = tc * 32 + (l & 31);
     if (row < M && col < r) {
       const float y = (row_mask && row_mask[row] == 0) ? 0.0f : scale * sum;   // masked rows: exact zeros
-      T[size_t(row) * r + col] = __builtin_bit_cast(uint16_t, (__bf16)y);
+      const __bf16 yb = (__bf16)y;
+      T[size_t(row) * r + col] = __builtin_bit_cast(uint16_t, yb);
+      if (jo.Tt) {
+        const float yt = jo.tscale == 1.0f ? float(yb) : jo.tscale * float(yb);
+        jo.Tt[size_t(col) * M + row] = __builtin_bit_cast(uint16_t, (__bf16)yt);
+      }
     }
   }
 }
@@ -793,10 +835,33 @@ void launch_skinny(const SkinnyParams& p, hipStream_t stream) {
 // accesses otherwise.
 constexpr int TP = 64, TP_PITCH = TP + 8;
 
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* src, int R, int C, uint16_t* dst,
-                                                         const uint8_t* row_mask, float scale, int vec) {
+// Several transposes in one launch: workgroup b takes tile b - first of the job
+// whose tiles [first, first + tiles) hold b (one launch instead of one per
+// transpose, each of which paid a launch and a memory round trip).
+struct TpJob {
+  const uint16_t* src;
+  uint16_t* dst;
+  const uint8_t* row_mask;
+  float scale;
+  int R, C, vec, tiles_x, first;
+};
+struct TpJobs {
+  TpJob j[5];
+  int n;
+};
+
+__global__ __launch_bounds__(256) void transpose_kernel(TpJobs jobs) {
   __shared__ uint16_t t[TP][TP_PITCH];
-  const int r0 = blockIdx.y * TP, c0 = blockIdx.x * TP;
+  int jb = 0;
+  while (jb + 1 < jobs.n && int(blockIdx.x) >= jobs.j[jb + 1].first) ++jb;
+  const TpJob& jo = jobs.j[jb];
+  const uint16_t* src = jo.src;
+  uint16_t* dst = jo.dst;
+  const uint8_t* row_mask = jo.row_mask;
+  const float scale = jo.scale;
+  const int R = jo.R, C = jo.C, vec = jo.vec;
+  const int tb = int(blockIdx.x) - jo.first;
+  const int r0 = (tb / jo.tiles_x) * TP, c0 = (tb % jo.tiles_x) * TP;
   const int tid = threadIdx.x, lr = tid >> 3, lc = (tid & 7) * 8;
   auto cvt = [&](uint16_t h, bool keep) -> uint16_t {
     if (!keep) return 0;
@@ -843,19 +908,57 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* src, int
   }
 }
 
+// Up to five transposes dst [C, R] = src [R, C]^T in one launch (see transpose_kernel).
+struct Transposes {
+  TpJobs jobs{};
+  int tiles = 0;
+  void add(const uint16_t* src, int R, int C, uint16_t* dst, const uint8_t* row_mask, float scale) {
+    TpJob& j = jobs.j[jobs.n++];
+    j.src = src;
+    j.dst = dst;
+    j.row_mask = row_mask;
+    j.scale = scale;
+    j.R = R;
+    j.C = C;
+    j.vec = (R % 8 == 0 && C % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
+             reinterpret_cast<uintptr_t>(dst) % 16 == 0) ? 1 : 0;
+    j.tiles_x = (C + TP - 1) / TP;
+    j.first = tiles;
+    tiles += j.tiles_x * ((R + TP - 1) / TP);
+  }
+  void launch(hipStream_t stream) const {
+    if (tiles > 0) hipLaunchKernelGGL(transpose_kernel, dim3(tiles), dim3(256), 0, stream, jobs);
+  }
+};
+
 void launch_transpose(const uint16_t* src, int R, int C, uint16_t* dst, const uint8_t* row_mask, float scale,
                       hipStream_t stream) {
-  const int vec = (R % 8 == 0 && C % 8 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(dst) % 16 == 0) ? 1 : 0;
-  dim3 grid((C + TP - 1) / TP, (R + TP - 1) / TP);
-  hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, stream, src, R, C, dst, row_mask, scale, vec);
+  Transposes t;
+  t.add(src, R, C, dst, row_mask, scale);
+  t.launch(stream);
+}
+
+LdJob lora_down_job(const uint16_t* X, const uint16_t* A, int M, int K, int r, float scale, uint16_t* T,
+                    const uint8_t* row_mask, uint16_t* Tt = nullptr, float tscale = 1.0f) {
+  LdJob j{X, A, M, K, r, scale, T, row_mask, Tt, tscale, ((M + 31) / 32) * ((r + 31) / 32)};
+  return j;
+}
+
+void launch_lora_downs(const LdJob* jobs, int n, hipStream_t stream) {
+  LdJobs js{};
+  int tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    js.j[i] = jobs[i];
+    tiles += jobs[i].tiles;
+  }
+  js.n = n;
+  if (tiles > 0) hipLaunchKernelGGL(lora_down_kernel, dim3(tiles), dim3(LD_WAVES * 64), 0, stream, js);
 }
 
 void launch_lora_down(const uint16_t* X, const uint16_t* A, int M, int K, int r, float scale, uint16_t* T,
                       const uint8_t* row_mask, hipStream_t stream) {
-  const unsigned tiles = unsigned((M + 31) / 32) * unsigned((r + 31) / 32);
-  hipLaunchKernelGGL(lora_down_kernel, dim3(tiles), dim3(LD_WAVES * 64), 0, stream, X, A, M, K, r, scale, T,
-                     row_mask);
+  const LdJob j = lora_down_job(X, A, M, K, r, scale, T, row_mask);
+  launch_lora_downs(&j, 1, stream);
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -863,7 +966,20 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 template <class C>
 void launch_cfg(const GemmParams& g, hipStream_t stream) {
   dim3 grid((g.N + C::BN - 1) / C::BN, (g.M + C::BM - 1) / C::BM, 1);
-  hipLaunchKernelGGL(gemm_kernel<C>, grid, dim3(C::THREADS), 0, stream, g);
+  hipLaunchKernelGGL(gemm_kernel<C>, grid, dim3(C::THREADS), 0, stream, g, g, 0);
+}
+
+// Two independent products in one launch on the square tiles.
+void launch_pair(const GemmParams& a, const GemmParams& b, hipStream_t stream) {
+  using C = CfgSquare;
+  const int ta = ((a.N + C::BN - 1) / C::BN) * ((a.M + C::BM - 1) / C::BM);
+  const int tb = ((b.N + C::BN - 1) / C::BN) * ((b.M + C::BM - 1) / C::BM);
+  if (ta == 0 || tb == 0) {
+    if (ta > 0) launch_cfg<C>(a, stream);
+    if (tb > 0) launch_cfg<C>(b, stream);
+    return;
+  }
+  hipLaunchKernelGGL(gemm_kernel<C>, dim3(ta + tb), dim3(C::THREADS), 0, stream, a, b, ta);
 }
 
 // Wide tiles when they fill the machine in whole waves of workgroups (or many
@@ -1032,18 +1148,30 @@ hipError_t launch_gemm_bwd(const GemmBwdArgs& a, hipStream_t stream) {
   const uint16_t* A = static_cast<const uint16_t*>(a.A);
   const uint16_t* B = static_cast<const uint16_t*>(a.B);
   const uint16_t* dY = static_cast<const uint16_t*>(a.dY);
-  // T = X A^T (unscaled, every row); U = bf16(s diag(m) dY B) through B^T
-  launch_lora_down(X, A, M, K, r, 1.0f, w.t, nullptr, stream);
-  launch_transpose(B, N, r, w.bt, nullptr, 1.0f, stream);
-  launch_lora_down(dY, w.bt, M, N, r, a.scale, w.u, a.row_mask, stream);
-  // dX = [dY | U] [W^T | A^T]^T
-  if (a.dX) {
-    const uint16_t* wt = static_cast<const uint16_t*>(a.Wt);
-    if (!wt) {
-      launch_transpose(W, N, K, w.wt, nullptr, 1.0f, stream);
-      wt = w.wt;
+  const uint16_t* wt = static_cast<const uint16_t*>(a.Wt);
+  // 1. The input transposes, one launch: B^T for U; A^T (and W^T when not given)
+  //    for dX; X^T for dA; (diag(m) dY)^T for dB (masked rows zeroed on the way).
+  {
+    Transposes t;
+    t.add(B, N, r, w.bt, nullptr, 1.0f);
+    if (a.dX) {
+      t.add(A, r, K, w.at, nullptr, 1.0f);
+      if (!wt) t.add(W, N, K, w.wt, nullptr, 1.0f);
     }
-    launch_transpose(A, r, K, w.at, nullptr, 1.0f, stream);
+    t.add(X, M, K, w.xt, nullptr, 1.0f);
+    t.add(dY, M, N, w.dyt, a.row_mask, 1.0f);
+    t.launch(stream);
+    if (a.dX && !wt) wt = w.wt;
+  }
+  // 2. T = X A^T (unscaled, every row) and U = bf16(s diag(m) dY B), one launch;
+  //    their epilogues also write (s T)^T and U^T for dB and dA.
+  {
+    const LdJob jobs[2] = {lora_down_job(X, A, M, K, r, 1.0f, w.t, nullptr, w.tt, a.scale),
+                           lora_down_job(dY, w.bt, M, N, r, a.scale, w.u, a.row_mask, w.ut, 1.0f)};
+    launch_lora_downs(jobs, 2, stream);
+  }
+  // 3. dX = [dY | U] [W^T | A^T]^T
+  if (a.dX) {
     GemmParams g{};
     g.seg[0] = Seg{dY, wt, N};
     g.seg[1] = Seg{w.u, w.at, r};
@@ -1053,29 +1181,22 @@ hipError_t launch_gemm_bwd(const GemmBwdArgs& a, hipStream_t stream) {
     g.y = static_cast<uint16_t*>(a.dX);
     launch_main(g, stream);
   }
-  // dA = U^T X: rows of U^T against rows of X^T, reduction over M
-  launch_transpose(w.u, M, r, w.ut, nullptr, 1.0f, stream);
-  launch_transpose(X, M, K, w.xt, nullptr, 1.0f, stream);
+  // 4. dA = U^T X (rows of U^T against rows of X^T, reduction over M) and dB =
+  //    (diag(m) dY)^T (s T), one launch.
   {
-    GemmParams g{};
-    g.seg[0] = Seg{w.ut, w.xt, M};
-    g.nseg = 1;
-    g.M = r;
-    g.N = K;
-    g.y = static_cast<uint16_t*>(a.dA);
-    launch_main(g, stream);
-  }
-  // dB = (diag(m) dY)^T (s T): masked rows of dY and the scale go in with the transposes
-  launch_transpose(dY, M, N, w.dyt, a.row_mask, 1.0f, stream);
-  launch_transpose(w.t, M, r, w.tt, nullptr, a.scale, stream);
-  {
-    GemmParams g{};
-    g.seg[0] = Seg{w.dyt, w.tt, M};
-    g.nseg = 1;
-    g.M = N;
-    g.N = r;
-    g.y = static_cast<uint16_t*>(a.dB);
-    launch_main(g, stream);
+    GemmParams ga{};
+    ga.seg[0] = Seg{w.ut, w.xt, M};
+    ga.nseg = 1;
+    ga.M = r;
+    ga.N = K;
+    ga.y = static_cast<uint16_t*>(a.dA);
+    GemmParams gb{};
+    gb.seg[0] = Seg{w.dyt, w.tt, M};
+    gb.nseg = 1;
+    gb.M = N;
+    gb.N = r;
+    gb.y = static_cast<uint16_t*>(a.dB);
+    launch_pair(ga, gb, stream);
   }
   return hipGetLastError();
 }
