@@ -56,9 +56,9 @@ COPY_BYTES = 1 << 30            # size of the calibration copy
 # sampler that makes the verifier's draft tokens).
 KERNEL_FUNCTIONS = {
     "verify": ("verify_kernel",),
-    "gated_lora_attn_4096x4096": ("gemm_kernel", "lora_down_kernel", "skinny_kernel"),
-    "gated_lora_mlp_4096x12288": ("gemm_kernel", "lora_down_kernel", "skinny_kernel"),
-    "tv": ("tv_kernel", "tv_count_kernel"),
+    "gated_lora_attn_4096x4096": ("gemm_kernel", "lora_down_kernel", "skinny_kernel", "skinny2_kernel"),
+    "gated_lora_mlp_4096x12288": ("gemm_kernel", "lora_down_kernel", "skinny_kernel", "skinny2_kernel"),
+    "tv": ("tv_kernel", "tv_pipe_kernel", "tv_count_kernel"),
 }
 
 # Source file of each timed entry point (the traffic summary is tied to its hash).
@@ -89,6 +89,8 @@ def parse():
                     help="run one kernel alone (for counter runs) and print its timing")
     ap.add_argument("--summarize-pmc", metavar="DIR", help="write profiles/KERNEL_traffic.md from counter CSVs")
     ap.add_argument("--kernel", help="timed entry point the counter CSVs belong to (with --summarize-pmc)")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("CSV", "NAME", "COMMAND"),
+                    help="write profiles/NAME_kernel_trace.md from a rocprofv3 kernel_trace.csv made by COMMAND")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="minimum CPU time spent on the oracle sample")
     return ap.parse_args()
@@ -362,8 +364,41 @@ def summarize_pmc(directory, name):
     print(out)
 
 
+def summarize_trace(csv_path, name, command):
+    """profiles/NAME_kernel_trace.md from a rocprofv3 --kernel-trace CSV: per kernel and
+    grid, the dispatch count and the mean, median, min and max duration."""
+    import statistics
+    groups = {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            kname = row["Kernel_Name"]
+            if "uno::" not in kname:
+                continue                        # PyTorch's kernels that make the inputs
+            head = kname.split("(uno::")[0] if "(uno::" in kname else kname
+            short = head.replace("void ", "").replace("uno::(anonymous namespace)::", "").replace("uno::", "")
+            wgs = int(row["Grid_Size_X"]) // max(1, int(row["Workgroup_Size_X"]))
+            key = (short, f"{wgs} x {row['Grid_Size_Y']}")
+            groups.setdefault(key, []).append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+    out = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"{name}_kernel_trace.md")
+    with open(out, "w") as f:
+        f.write(f"# Kernel durations: {name} (rocprofv3 kernel trace)\n\n")
+        f.write("Command (repository root R on the GPU box; `cd /tmp && export TMPDIR=/tmp` first):\n\n")
+        f.write(f"    {command}\n")
+        f.write(f"    python3 bench.py --summarize-trace <kernel_trace.csv> {name} '<the command above>'\n\n")
+        f.write("Library kernels only (PyTorch's input generation left out), by kernel and grid\n"
+                "(workgroups x grid y); durations in microseconds.\n\n")
+        f.write("| Kernel | Grid | Dispatches | Mean | Median | Min | Max |\n|---|---|---|---|---|---|---|\n")
+        for (k, g), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            f.write(f"| `{k}` | {g} | {len(v)} | {statistics.fmean(v):.1f} | {statistics.median(v):.1f} | "
+                    f"{min(v):.1f} | {max(v):.1f} |\n")
+    print(out)
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
     if args.summarize_pmc:
         if args.kernel not in KERNEL_SOURCES:
             raise SystemExit(f"--kernel must be one of {sorted(KERNEL_SOURCES)}")
