@@ -91,6 +91,8 @@ def parse():
     ap.add_argument("--kernel", help="timed entry point the counter CSVs belong to (with --summarize-pmc)")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("CSV", "NAME", "COMMAND"),
                     help="write profiles/NAME_kernel_trace.md from a rocprofv3 kernel_trace.csv made by COMMAND")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="run the step back to back this long before the warm-up steps (clock ramp)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="minimum CPU time spent on the oracle sample")
     return ap.parse_args()
@@ -439,6 +441,18 @@ def main():
             fn()
         verify_run()
 
+    # Clock settle: from an idle GPU the first steps run slow while the clock
+    # ramps (measured: 453 us per step over the first 10 steps, 297 us by the
+    # 30th, 270 us from about 25 ms on). The step runs back to back for
+    # --settle-ms before the warm-up steps, so the timed steps see the clock of a
+    # GPU kept busy, as in a serving loop. Reported in the JSON line.
+    settle_steps = 0
+    t_settle = time.perf_counter() + args.settle_ms / 1000.0
+    while time.perf_counter() < t_settle:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        settle_steps += 20
     # Headline: the step as a caller runs it, timed only at its boundaries (events
     # between the calls would each add a fence to the stream).
     for _ in range(args.warmup):
@@ -520,6 +534,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"ms": args.settle_ms, "steps": settle_steps},
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",

@@ -184,3 +184,22 @@ def test_alternating_shapes_share_the_workspace():
     for _ in range(2):
         for (args, mask), ref in zip(reversed(runs), reversed(first)):
             np.testing.assert_array_equal(_bits(_run(*args, mask, 16.0)), ref)
+
+
+# Tile-row shapes of the tiled path: ragged rows, columns, reduction and rank
+# (a rank that is not a multiple of 32), many reduction tiles per column tile, and
+# the wide tiles with ragged edges.
+ROW_TILE_SHAPES = [
+    (1000, 1032, 1100, 72),     # square tiles 8 x 9
+    (256, 4096, 1024, 32),      # 8 column tiles, 32 reduction tiles
+    (300, 512, 2048, 64),       # 16 column tiles, 4 reduction tiles
+    (1000, 1024, 12280, 128),   # wide tiles 4 x 64, ragged rows and columns
+]
+
+
+@pytest.mark.parametrize("M,K,N,r", ROW_TILE_SHAPES)
+def test_row_tile_shapes(M, K, N, r):
+    mask = (np.random.default_rng(M + K + N).random(M) < 0.8).astype(np.uint8)
+    rows = None if M * N * K <= 2e9 else np.random.default_rng(1).choice(M, 96, replace=False)
+    print(f"tiled gated LoRA M={M} K={K} N={N} r={r}", flush=True)
+    _check_case(M, K, N, r, 16.0, mask, rows=rows)
