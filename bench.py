@@ -510,7 +510,7 @@ def main():
 
     tv_leg = None
     if not args.no_tv:
-        tv_leg = tv_benchmark(uno, workloads, dev, max(3, args.steps // 4))
+        tv_leg = tv_benchmark(uno, workloads, dev, max(10, args.steps // 4))
 
     legs = None
     if not args.no_legs:
@@ -594,6 +594,8 @@ def tv_benchmark(uno, workloads, dev, iters):
         if e.status != "UNO_ERR_UNSUPPORTED":
             raise
         return {"status": "not built"}
+    for _ in range(2):
+        uno.uno_tv_loss_fwd_bwd(t, s, mask, c["temperature"], want_rows=False)
     torch.cuda.synchronize()
     n_resp = int(mask.sum().item())
     timer = KernelTimer()

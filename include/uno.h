@@ -225,7 +225,9 @@ int uno_gated_lora_linear(const void* X, const void* W, const void* A, const voi
  *   dX : bf16 [M, K] (out, optional: NULL skips it); dA : bf16 [r, K] (out);
  *   dB : bf16 [N, r] (out); outputs must not alias inputs or each other
  *   workspace : >= uno_gated_lora_linear_bwd_workspace(M, N, K, r) bytes (it
- *   holds transposed copies of W, X, dY and the rank-r factors)
+ *   holds transposed copies of W, X, dY and the rank-r factors, and counters of
+ *   the reduction slices that each call leaves zero: zero it once with
+ *   uno_workspace_init before its first use)
  * Limits: M, N, K, r >= 1; M, N, K and r multiples of 8 and all row starts
  * 16-byte aligned (UNO_ERR_UNSUPPORTED otherwise).
  * ------------------------------------------------------------------------- */

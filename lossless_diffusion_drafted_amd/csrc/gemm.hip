@@ -23,6 +23,7 @@
 
 #include "../../include/uno.h"
 
+#include <algorithm>
 #include <climits>
 #include "common.h"
 #include "kernels.h"
@@ -259,16 +260,25 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmPar
 }
 
 // LoRA-down T = bf16(scale * X A^T), X [M, K], A [r, K], T [M, r].
-// One workgroup per 32 x 32 tile of T, over the whole reduction, so no
-// workgroup waits for another and the sum order is fixed. Wave w of the 8 takes
-// a contiguous 1/8 of K in chunks of 64: its lanes load a chunk of the 32 X rows
-// and the 32 A rows with row-contiguous 16-byte loads (8 lanes per 128-byte row
-// segment), write it to the wave's own LDS tiles and read it back as MFMA
-// fragments, while the next three chunks' loads are in flight (the loop is
-// latency-bound otherwise). LDS operations of one
-// wave execute in order, so the wave needs no barrier. The wave partials are
-// summed in LDS in wave order, scaled and rounded.
+// One workgroup per 32 x 32 tile of T and slice of the reduction. Wave w of the 8
+// takes a contiguous 1/8 of its slice in chunks of 64: its lanes load a chunk of
+// the 32 X rows and the 32 A rows with row-contiguous 16-byte loads (8 lanes per
+// 128-byte row segment), write it to the wave's own LDS tiles and read it back as
+// MFMA fragments, while the next three chunks' loads are in flight (the loop is
+// latency-bound otherwise). LDS operations of one wave execute in order, so the
+// wave needs no barrier. The wave partials are summed in LDS in wave order.
+//   With one slice the workgroup scales, rounds and stores its tile. With KS
+// slices (a job whose reduction is KS times another's in the same launch, so that
+// its workgroups take as long) each slice stores its fp32 tile with
+// device-coherent stores and takes a ticket; the last slice of the tile to
+// finish adds the KS tiles in slice order (the sum order is fixed), stores T and
+// clears the ticket.
+//   Xt, when given, receives X^T [K, M] (rows with mask 0 zeroed when a row mask
+// is given) from the chunks already in LDS: each of the tile's column-tile
+// workgroups writes a quarter of each chunk's 64 k-rows, 64 contiguous bytes per
+// k-row, so X is not read again for it.
 constexpr int LD_WAVES = 8, LD_KC = 64, LD_PITCH = LD_KC + 8;   // pitch: bf16 per LDS row
+constexpr int LD_MAX_SLICES = 8;
 
 // One LoRA-down product of a launch (a launch may carry two: the backward's T and U).
 // Tt, when given, also receives the transposed tile, bf16(tscale * T) [r, M].
@@ -281,7 +291,11 @@ struct LdJob {
   const uint8_t* row_mask;
   uint16_t* Tt;
   float tscale;
-  int tiles;
+  int tiles;             // 32 x 32 tiles of T
+  int ks;                // reduction slices per tile (1..LD_MAX_SLICES)
+  float* part;           // [tiles, ks, 32 * 32] fp32 slice tiles (ks > 1)
+  unsigned* ticket;      // [tiles], zero on entry and on exit (ks > 1)
+  uint16_t* Xt;          // X^T [K, M] or null
 };
 struct LdJobs {
   LdJob j[2];
@@ -293,20 +307,23 @@ __global__ __launch_bounds__(LD_WAVES * 64) void lora_down_kernel(LdJobs jobs) {
   constexpr int STAGE_BYTES = LD_WAVES * 2 * TILE * 2;
   constexpr int RED_BYTES = LD_WAVES * 16 * 64 * 4;
   __shared__ __attribute__((aligned(16))) char smem[STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES];
-  // Tiles of the same 32 X rows go to consecutive ids on one XCD (workgroups
-  // are dealt to the 8 XCDs round robin), so each XCD's L2 fetches those rows once.
+  __shared__ int s_last;
+  // Workgroups of the same 32 X rows and slice go to consecutive ids on one XCD
+  // (workgroups are dealt to the 8 XCDs round robin), so each XCD's L2 fetches
+  // those rows once.
   int tid_x = xcd_contiguous_id(int(blockIdx.x), int(gridDim.x));
-  const int jb = (jobs.n > 1 && tid_x >= jobs.j[0].tiles) ? 1 : 0;
+  const int jb = (jobs.n > 1 && tid_x >= jobs.j[0].tiles * jobs.j[0].ks) ? 1 : 0;
   const LdJob& jo = jobs.j[jb];
-  if (jb) tid_x -= jobs.j[0].tiles;
+  if (jb) tid_x -= jobs.j[0].tiles * jobs.j[0].ks;
   const uint16_t* X = jo.X;
   const uint16_t* A = jo.A;
-  const int M = jo.M, K = jo.K, r = jo.r;
+  const int M = jo.M, K = jo.K, r = jo.r, ks = jo.ks;
   const float scale = jo.scale;
   uint16_t* T = jo.T;
   const uint8_t* row_mask = jo.row_mask;
   const int ttc = (r + 31) / 32;
-  const int tm = tid_x / ttc, tc = tid_x % ttc;
+  const int tc = tid_x % ttc, sl = (tid_x / ttc) % ks, tm = tid_x / (ttc * ks);
+  const int tile = tm * ttc + tc;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem) + wave * 2 * TILE;
   uint16_t* as = xs + TILE;
@@ -314,8 +331,10 @@ __global__ __launch_bounds__(LD_WAVES * 64) void lora_down_kernel(LdJobs jobs) {
   const __amdgpu_buffer_rsrc_t ra = make_row_rsrc(A, uint32_t(size_t(r) * K * 2));
   // Loads: lane l covers rows l / 8 + 8 j (j < 4) at k offset 8 (l % 8).
   const int lr = lane >> 3, lk = (lane & 7) * 8;
-  const int kw = (K + LD_WAVES * LD_KC - 1) / (LD_WAVES * LD_KC) * LD_KC;
-  const int kb = wave * kw, ke = min(K, kb + kw);
+  const int klen = (K + ks * LD_KC - 1) / (ks * LD_KC) * LD_KC;        // slice length
+  const int k0 = sl * klen, k1 = min(K, k0 + klen);
+  const int kw = (klen + LD_WAVES * LD_KC - 1) / (LD_WAVES * LD_KC) * LD_KC;
+  const int kb = k0 + wave * kw, ke = min(k1, kb + kw);
   constexpr int NB = 4;                               // chunks in flight
   u32x4_t xv[NB][4], av[NB][4];
   auto load = [&](int k, u32x4_t (&xb)[4], u32x4_t (&ab)[4]) {
@@ -329,6 +348,43 @@ __global__ __launch_bounds__(LD_WAVES * 64) void lora_down_kernel(LdJobs jobs) {
           ra, (in && arow < r) ? uint32_t((size_t(arow) * K + k + lk) * 2) : kOutOfRange, 0u, 0);
     }
   };
+  // The transposed copy: in each chunk, pass p (k-rows 16 p .. 16 p + 15) belongs
+  // to column tile p % ttc. Lane l takes k-row 16 p + l / 4 and the 8 X rows
+  // 8 (l % 4) .. + 7 of the tile: one 16-byte store.
+  const bool xt_on = jo.Xt != nullptr && tc < 4;
+  const int xt_row = 8 * (lane & 3);
+  uint32_t xt_keep = 0xffu;                           // per lane: which of its 8 rows survive the mask
+  if (xt_on) {
+    xt_keep = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = tm * 32 + xt_row + e;
+      if (row < M && (row_mask == nullptr || row_mask[row] != 0)) xt_keep |= 1u << e;
+    }
+  }
+  // The mask bytes above were read with ordinary loads: retire them so the
+  // chunk loads are the only loads counted below.
+  wait_vmcnt<0>();
+  auto write_xt = [&](int k) {
+    for (int p = tc; p < 4; p += ttc) {
+      const int kr = 16 * p + (lane >> 2);
+      if (k + kr >= ke) continue;
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = ((xt_keep >> (2 * e)) & 1u) ? xs[(xt_row + 2 * e) * LD_PITCH + kr] : 0u;
+        const uint32_t hi = ((xt_keep >> (2 * e + 1)) & 1u) ? xs[(xt_row + 2 * e + 1) * LD_PITCH + kr] : 0u;
+        w[e] = lo | (hi << 16);
+      }
+      const int row0 = tm * 32 + xt_row;
+      uint16_t* dst = jo.Xt + size_t(k + kr) * M + row0;
+      if (row0 + 8 <= M && (M % 8) == 0) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+        for (int e = 0; e < 8 && row0 + e < M; ++e) dst[e] = uint16_t(w[e / 2] >> (16 * (e & 1)));
+      }
+    }
+  };
   f32x16_t acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
@@ -337,10 +393,10 @@ __global__ __launch_bounds__(LD_WAVES * 64) void lora_down_kernel(LdJobs jobs) {
 #pragma unroll
   for (int b = 0; b < NB - 1; ++b) load(kb + b * LD_KC, xv[b], av[b]);
   // Chunks past the range load zeros (out of range) and add nothing.
-  for (int k0 = kb; k0 < ke; k0 += NB * LD_KC) {
+  for (int k0c = kb; k0c < ke; k0c += NB * LD_KC) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int k = k0 + b * LD_KC;
+      const int k = k0c + b * LD_KC;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         *reinterpret_cast<u32x4_t*>(xs + (lr + 8 * j) * LD_PITCH + lk) = xv[b][j];
@@ -348,11 +404,12 @@ __global__ __launch_bounds__(LD_WAVES * 64) void lora_down_kernel(LdJobs jobs) {
       }
       load(k + (NB - 1) * LD_KC, xv[(b + NB - 1) % NB], av[(b + NB - 1) % NB]);
 #pragma unroll
-      for (int ks = 0; ks < LD_KC / 16; ++ks) {
-        const bf16x8_t xf = *reinterpret_cast<const bf16x8_t*>(xs + fo + ks * 16);
-        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(as + fo + ks * 16);
+      for (int kk = 0; kk < LD_KC / 16; ++kk) {
+        const bf16x8_t xf = *reinterpret_cast<const bf16x8_t*>(xs + fo + kk * 16);
+        const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(as + fo + kk * 16);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf, af, acc, 0, 0, 0);
       }
+      if (xt_on && k < ke) write_xt(k);
     }
   }
   __syncthreads();                                    // the stage tiles become the reduction buffer
@@ -361,11 +418,7 @@ __global__ __launch_bounds__(LD_WAVES * 64) void lora_down_kernel(LdJobs jobs) {
   for (int v = 0; v < 16; ++v) red[(wave * 16 + v) * 64 + lane] = acc[v];
   __syncthreads();
   // Accumulator v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
-  for (int i = threadIdx.x; i < 16 * 64; i += LD_WAVES * 64) {
-    const int v = i >> 6, l = i & 63;
-    float sum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < LD_WAVES; ++w) sum += red[(w * 16 + v) * 64 + l];
+  auto store_t = [&](int v, int l, float sum) {
     const int row = tm * 32 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3), col = tc * 32 + (l & 31);
     if (row < M && col < r) {
       const float y = (row_mask && row_mask[row] == 0) ? 0.0f : scale * sum;   // masked rows: exact zeros
@@ -376,7 +429,50 @@ __global__ __launch_bounds__(LD_WAVES * 64) void lora_down_kernel(LdJobs jobs) {
         jo.Tt[size_t(col) * M + row] = __builtin_bit_cast(uint16_t, (__bf16)yt);
       }
     }
+  };
+  if (ks == 1) {
+    for (int i = threadIdx.x; i < 16 * 64; i += LD_WAVES * 64) {
+      const int v = i >> 6, l = i & 63;
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < LD_WAVES; ++w) sum += red[(w * 16 + v) * 64 + l];
+      store_t(v, l, sum);
+    }
+    return;
   }
+  // Slice tile in accumulator order [v][lane], device-coherent stores.
+  float* part = jo.part + (size_t(tile) * ks + sl) * 1024;
+  for (int i = threadIdx.x; i < 16 * 64; i += LD_WAVES * 64) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < LD_WAVES; ++w) sum += red[w * 1024 + i];
+    __hip_atomic_store(&part[i], sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // Every lane's device-coherent stores are complete before the ticket is taken.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(&jo.ticket[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old == unsigned(ks - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // The slice tiles with device-coherent loads, all issued before the first is
+  // summed, then added in slice order.
+  const __amdgpu_buffer_rsrc_t rp = make_row_rsrc(jo.part + size_t(tile) * ks * 1024, uint32_t(ks * 1024 * 4));
+  for (int i = threadIdx.x; i < 16 * 64; i += LD_WAVES * 64) {
+    float v[LD_MAX_SLICES];
+#pragma unroll
+    for (int q = 0; q < LD_MAX_SLICES; ++q)
+      v[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+          rp, q < ks ? uint32_t((q * 1024 + i) * 4) : kOutOfRange, 0u, kBufDeviceCoherent));
+    float sum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < LD_MAX_SLICES; ++q)
+      if (q < ks) sum += v[q];
+    store_t(i >> 6, i & 63, sum);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(&jo.ticket[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -939,9 +1035,19 @@ void launch_transpose(const uint16_t* src, int R, int C, uint16_t* dst, const ui
 }
 
 LdJob lora_down_job(const uint16_t* X, const uint16_t* A, int M, int K, int r, float scale, uint16_t* T,
-                    const uint8_t* row_mask, uint16_t* Tt = nullptr, float tscale = 1.0f) {
-  LdJob j{X, A, M, K, r, scale, T, row_mask, Tt, tscale, ((M + 31) / 32) * ((r + 31) / 32)};
+                    const uint8_t* row_mask, uint16_t* Tt = nullptr, float tscale = 1.0f, uint16_t* Xt = nullptr) {
+  LdJob j{X, A, M, K, r, scale, T, row_mask, Tt, tscale, ((M + 31) / 32) * ((r + 31) / 32), 1, nullptr, nullptr, Xt};
   return j;
+}
+
+// Reduction slices for two jobs of one launch: the longer reduction is cut into
+// about as many slices as it is times the shorter, so that the workgroups of both
+// take about as long.
+void balance_slices(LdJob& a, LdJob& b) {
+  const int kmin = a.K < b.K ? a.K : b.K;
+  if (kmin <= 0) return;
+  a.ks = std::min(LD_MAX_SLICES, std::max(1, (a.K + kmin / 2) / kmin));
+  b.ks = std::min(LD_MAX_SLICES, std::max(1, (b.K + kmin / 2) / kmin));
 }
 
 void launch_lora_downs(const LdJob* jobs, int n, hipStream_t stream) {
@@ -949,7 +1055,7 @@ void launch_lora_downs(const LdJob* jobs, int n, hipStream_t stream) {
   int tiles = 0;
   for (int i = 0; i < n; ++i) {
     js.j[i] = jobs[i];
-    tiles += jobs[i].tiles;
+    tiles += jobs[i].tiles * jobs[i].ks;
   }
   js.n = n;
   if (tiles > 0) hipLaunchKernelGGL(lora_down_kernel, dim3(tiles), dim3(LD_WAVES * 64), 0, stream, js);
@@ -1108,12 +1214,34 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
 // workspace, with the row mask and the scale applied by the transposes where the
 // formula puts them.
 namespace {
+// Backward workspace: [tickets (64 KB, zero between calls, first so that they keep
+// their place across shapes)] [T] [B^T] [U] [W^T] [A^T] [U^T] [X^T] [dY^T] [T^T]
+// [LoRA-down slice tiles].
 struct BwdWs {
+  unsigned* tickets;
   uint16_t *t, *bt, *u, *wt, *at, *ut, *xt, *dyt, *tt;
+  float* part;
 };
+// The backward's two LoRA-downs, T = X A^T and U = s diag(m) dY B, with their
+// slices balanced; the slice tiles' size in bytes.
+void bwd_lora_jobs(int M, int N, int K, int r, LdJob& jt, LdJob& ju) {
+  jt = lora_down_job(nullptr, nullptr, M, K, r, 1.0f, nullptr, nullptr);
+  ju = lora_down_job(nullptr, nullptr, M, N, r, 1.0f, nullptr, nullptr);
+  if (size_t(jt.tiles) + ju.tiles <= kTicketBytes / 4) balance_slices(jt, ju);
+}
+size_t bwd_part_bytes(int M, int N, int K, int r) {
+  LdJob jt, ju;
+  bwd_lora_jobs(M, N, K, r, jt, ju);
+  size_t n = 0;
+  if (jt.ks > 1) n += size_t(jt.tiles) * jt.ks * 1024 * 4;
+  if (ju.ks > 1) n += size_t(ju.tiles) * ju.ks * 1024 * 4;
+  return align256(n);
+}
 BwdWs bwd_ws(void* ws, int M, int N, int K, int r) {
   char* c = static_cast<char*>(ws);
   BwdWs w;
+  w.tickets = reinterpret_cast<unsigned*>(c);
+  c += kTicketBytes;
   auto take = [&](size_t elems) {
     uint16_t* p = reinterpret_cast<uint16_t*>(c);
     c += align256(elems * 2);
@@ -1128,6 +1256,7 @@ BwdWs bwd_ws(void* ws, int M, int N, int K, int r) {
   w.xt = take(size_t(K) * M);
   w.dyt = take(size_t(N) * M);
   w.tt = take(size_t(r) * M);
+  w.part = reinterpret_cast<float*>(c);
   return w;
 }
 }  // namespace
@@ -1135,8 +1264,9 @@ BwdWs bwd_ws(void* ws, int M, int N, int K, int r) {
 size_t gemm_bwd_workspace_bytes(int M, int N, int K, int r) {
   if (M <= 0 || N <= 0 || K <= 0 || r <= 0) return 256;
   const size_t m = M, n = N, k = K, rr = r;
-  return align256(m * rr * 2) * 3 + align256(rr * n * 2) + align256(k * n * 2) + align256(k * rr * 2) +
-         align256(rr * m * 2) + align256(k * m * 2) + align256(n * m * 2);
+  return kTicketBytes + align256(m * rr * 2) * 3 + align256(rr * n * 2) + align256(k * n * 2) +
+         align256(k * rr * 2) + align256(rr * m * 2) + align256(k * m * 2) + align256(n * m * 2) +
+         bwd_part_bytes(M, N, K, r);
 }
 
 hipError_t launch_gemm_bwd(const GemmBwdArgs& a, hipStream_t stream) {
@@ -1149,8 +1279,8 @@ hipError_t launch_gemm_bwd(const GemmBwdArgs& a, hipStream_t stream) {
   const uint16_t* B = static_cast<const uint16_t*>(a.B);
   const uint16_t* dY = static_cast<const uint16_t*>(a.dY);
   const uint16_t* wt = static_cast<const uint16_t*>(a.Wt);
-  // 1. The input transposes, one launch: B^T for U; A^T (and W^T when not given)
-  //    for dX; X^T for dA; (diag(m) dY)^T for dB (masked rows zeroed on the way).
+  // 1. The weight transposes, one launch: B^T for U; A^T (and W^T when not given)
+  //    for dX.
   {
     Transposes t;
     t.add(B, N, r, w.bt, nullptr, 1.0f);
@@ -1158,16 +1288,29 @@ hipError_t launch_gemm_bwd(const GemmBwdArgs& a, hipStream_t stream) {
       t.add(A, r, K, w.at, nullptr, 1.0f);
       if (!wt) t.add(W, N, K, w.wt, nullptr, 1.0f);
     }
-    t.add(X, M, K, w.xt, nullptr, 1.0f);
-    t.add(dY, M, N, w.dyt, a.row_mask, 1.0f);
     t.launch(stream);
     if (a.dX && !wt) wt = w.wt;
   }
-  // 2. T = X A^T (unscaled, every row) and U = bf16(s diag(m) dY B), one launch;
-  //    their epilogues also write (s T)^T and U^T for dB and dA.
+  // 2. T = X A^T (unscaled, every row) and U = bf16(s diag(m) dY B), one launch,
+  //    the longer reduction in slices; their epilogues also write (s T)^T and U^T
+  //    for dB and dA, and their chunks X^T for dA and (diag(m) dY)^T for dB
+  //    (masked rows zeroed).
   {
-    const LdJob jobs[2] = {lora_down_job(X, A, M, K, r, 1.0f, w.t, nullptr, w.tt, a.scale),
-                           lora_down_job(dY, w.bt, M, N, r, a.scale, w.u, a.row_mask, w.ut, 1.0f)};
+    LdJob jobs[2];
+    bwd_lora_jobs(M, N, K, r, jobs[0], jobs[1]);
+    const int ks_t = jobs[0].ks, ks_u = jobs[1].ks;
+    jobs[0] = lora_down_job(X, A, M, K, r, 1.0f, w.t, nullptr, w.tt, a.scale, w.xt);
+    jobs[1] = lora_down_job(dY, w.bt, M, N, r, a.scale, w.u, a.row_mask, w.ut, 1.0f, w.dyt);
+    jobs[0].ks = ks_t;
+    jobs[1].ks = ks_u;
+    float* part = w.part;
+    for (int i = 0; i < 2; ++i) {
+      jobs[i].ticket = w.tickets + (i == 0 ? 0 : jobs[0].tiles);
+      if (jobs[i].ks > 1) {
+        jobs[i].part = part;
+        part += size_t(jobs[i].tiles) * jobs[i].ks * 1024;
+      }
+    }
     launch_lora_downs(jobs, 2, stream);
   }
   // 3. dX = [dY | U] [W^T | A^T]^T

@@ -73,6 +73,8 @@ def test_tiny_backward(scale):
     (8, 8, 8, 8),              # smallest
     (512, 1024, 640, 64),
     (136, 2560, 10240, 64),    # looped-model MLP shape, few rows
+    (200, 1000, 3000, 24),     # U's reduction in 3 slices, the last one short
+    (96, 3072, 1024, 40),      # T's reduction in 3 slices, a partial column tile
 ])
 def test_ragged_backward(M, K, N, r):
     mask = (np.random.default_rng(M + N).random(M) < 0.8).astype(np.uint8)
@@ -149,3 +151,28 @@ def test_backward_with_pretransposed_weight():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def test_backward_alternating_shapes_share_the_workspace():
+    """The reduction-slice counters live in the workspace and must be left clear:
+    shapes with different slice counts (U in 3, T in 3, none) alternate on one
+    workspace, and every repeat is bitwise identical (slices are summed in a fixed
+    order)."""
+    shapes = [(256, 1024, 3072, 32), (128, 3072, 1024, 64), (64, 512, 512, 16)]
+    runs = []
+    for M, K, N, r in shapes:
+        X, W, A, B = workloads.gemm_inputs(M, K, N, r, seed=9)
+        G = workloads.gemm_grad(M, N, seed=9)
+        runs.append(([to_device(a, DEV) for a in (G, X, W, A, B)],
+                     to_device(workloads.noise_row_mask(M // 8, 8), DEV)))
+
+    def once(args, mask):
+        out = [t.clone() for t in _uno().uno_gated_lora_linear_bwd(*args, mask, 4.0)]
+        torch.cuda.synchronize()
+        return [t.view(torch.int16).cpu() for t in out]
+
+    first = [once(*run) for run in runs]
+    for _ in range(2):
+        for run, ref in zip(reversed(runs), reversed(first)):
+            for a, b in zip(once(*run), ref):
+                assert torch.equal(a, b)
