@@ -1062,8 +1062,13 @@ void launch_lora_downs(const LdJob* jobs, int n, hipStream_t stream) {
 }
 
 void launch_lora_down(const uint16_t* X, const uint16_t* A, int M, int K, int r, float scale, uint16_t* T,
-                      const uint8_t* row_mask, hipStream_t stream) {
-  const LdJob j = lora_down_job(X, A, M, K, r, scale, T, row_mask);
+                      const uint8_t* row_mask, int ks, float* part, unsigned* tickets, hipStream_t stream) {
+  LdJob j = lora_down_job(X, A, M, K, r, scale, T, row_mask);
+  if (ks > 1) {
+    j.ks = ks;
+    j.part = part;
+    j.ticket = tickets;
+  }
   launch_lora_downs(&j, 1, stream);
 }
 
@@ -1118,6 +1123,15 @@ void launch_small(const SkinnyParams& p, hipStream_t stream) {
     launch_skinny(p, stream);
 }
 
+// Reduction slices of the forward's LoRA-down on the tiled path: two when the
+// tiles alone would leave CUs idle and their tickets fit the ticket area.
+// (Measured at the Qwen shapes, 128 tiles: two slices 1.8 us faster per call than
+// one; three and four, which take a second round of workgroups, 4-6 us slower.)
+int fwd_lora_slices(int M, int K, int r) {
+  const int tiles = ((M + 31) / 32) * ((r + 31) / 32);
+  return (tiles <= 128 && K >= 1024) ? 2 : 1;
+}
+
 size_t skinny_part_bytes(int M, int N, int K, int r) {
   int ks = small_slices(M, N, K), ks_r = r > 0 ? small_slices(M, r, K) : 1;
   size_t big = 0;
@@ -1131,8 +1145,11 @@ size_t skinny_part_bytes(int M, int N, int K, int r) {
 size_t gemm_workspace_bytes(int M, int N, int K, int r) {
   if (M <= 0 || N <= 0) return 256;
   size_t n = kTicketBytes + (r > 0 ? align256(size_t(M) * r * 2) : 0);
-  if (M <= 64 && K % SK_GROUP == 0 && r % 32 == 0) n += skinny_part_bytes(M, N, K, r);
-  return n;
+  // One region serves whichever path runs: the small-M slice tiles or the
+  // LoRA-down's slice tiles.
+  const size_t sk = (M <= 64 && K % SK_GROUP == 0 && r % 32 == 0) ? skinny_part_bytes(M, N, K, r) : 0;
+  const size_t ld = r > 0 ? align256(size_t((M + 31) / 32) * ((r + 31) / 32) * LD_MAX_SLICES * 1024 * 4) : 0;
+  return n + (sk > ld ? sk : ld);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
@@ -1188,7 +1205,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   const uint16_t* tmat = nullptr;
   if (a.r > 0) {
     launch_lora_down(static_cast<const uint16_t*>(a.X), static_cast<const uint16_t*>(a.A), a.M, a.K, a.r, a.scale,
-                     tws, nullptr, stream);
+                     tws, nullptr, fwd_lora_slices(a.M, a.K, a.r), part, tickets, stream);
     tmat = tws;
   }
   GemmParams g{};
