@@ -70,6 +70,7 @@ struct Cfg {
 // in 2 or 3 stages were 3-5% slower on 4096 -> 4096.
 using CfgWide = Cfg<256, 192, 64, 4, 2, 2>;    // 8 waves of 64 x 96
 using CfgSquare = Cfg<128, 128, 128, 2, 4, 2>; // 8 waves of 64 x 32
+using CfgHalf = Cfg<64, 128, 128, 2, 4, 2>;    // 8 waves of 32 x 32: short products on few tiles
 
 struct Seg {
   const uint16_t* a;   // [M, k] row-major (X or T)
@@ -1088,9 +1089,8 @@ void launch_cfg(const GemmParams& g, hipStream_t stream) {
   hipLaunchKernelGGL(gemm_kernel<C>, grid, dim3(C::THREADS), 0, stream, g, g, 0);
 }
 
-// Two independent products in one launch on the square tiles.
-void launch_pair(const GemmParams& a, const GemmParams& b, hipStream_t stream) {
-  using C = CfgSquare;
+template <class C>
+void launch_pair_cfg(const GemmParams& a, const GemmParams& b, hipStream_t stream) {
   const int ta = ((a.N + C::BN - 1) / C::BN) * ((a.M + C::BM - 1) / C::BM);
   const int tb = ((b.N + C::BN - 1) / C::BN) * ((b.M + C::BM - 1) / C::BM);
   if (ta == 0 || tb == 0) {
@@ -1099,6 +1099,19 @@ void launch_pair(const GemmParams& a, const GemmParams& b, hipStream_t stream) {
     return;
   }
   hipLaunchKernelGGL(gemm_kernel<C>, dim3(ta + tb), dim3(C::THREADS), 0, stream, a, b, ta);
+}
+
+// Two independent products in one launch: square tiles, or half-height tiles
+// when square ones would leave half the CUs idle (the backward's dA and dB at
+// 1024 rows: 128 square tiles).
+void launch_pair(const GemmParams& a, const GemmParams& b, hipStream_t stream) {
+  using C = CfgSquare;
+  const long tiles = long((a.N + C::BN - 1) / C::BN) * ((a.M + C::BM - 1) / C::BM) +
+                     long((b.N + C::BN - 1) / C::BN) * ((b.M + C::BM - 1) / C::BM);
+  if (tiles <= 128)
+    launch_pair_cfg<CfgHalf>(a, b, stream);
+  else
+    launch_pair_cfg<C>(a, b, stream);
 }
 
 // Wide tiles when they fill the machine in whole waves of workgroups (or many
