@@ -188,24 +188,34 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmPar
   const int fr = lane & 31, fh = lane >> 5;
   const int fswz = (fr / C::RS) % C::CPR;            // block bases are multiples of 32
   const int arow = (wm * C::WTM + fr) * C::CPR * 16, brow = (wn * C::WTN + fr) * C::CPR * 16;
+  // The fragments of step ks + 1 are read while step ks is multiplied (two
+  // register sets), so an MFMA does not wait for the LDS read issued just before it.
   auto compute = [&](int st) {
     const char* As = smem + st * C::STAGE_BYTES + arow;
     const char* Bs = smem + st * C::STAGE_BYTES + C::A_BYTES + brow;
-#pragma unroll
-    for (int ks = 0; ks < C::BK / 16; ++ks) {
+    bf16x8_t af[2][C::MI], bfr[2][C::NJ];
+    auto read = [&](int ks, int b) {
       const int ch = ((2 * ks + fh) ^ fswz) * 16;
-      bf16x8_t af[C::MI], bfr[C::NJ];
 #pragma unroll
       for (int i = 0; i < C::MI; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(As + i * 32 * C::CPR * 16 + ch);
+        af[b][i] = *reinterpret_cast<const bf16x8_t*>(As + i * 32 * C::CPR * 16 + ch);
 #pragma unroll
       for (int j = 0; j < C::NJ; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + j * 32 * C::CPR * 16 + ch);
+        bfr[b][j] = *reinterpret_cast<const bf16x8_t*>(Bs + j * 32 * C::CPR * 16 + ch);
+    };
+    read(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < C::BK / 16; ++ks) {
+      const int b = ks & 1;
+      if (ks + 1 < C::BK / 16) read(ks + 1, b ^ 1);
+      // (The scheduler would otherwise sink the reads back below the MFMAs.)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < C::MI; ++i)
 #pragma unroll
         for (int j = 0; j < C::NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[b][i], bfr[b][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
