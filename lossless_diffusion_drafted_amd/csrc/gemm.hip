@@ -36,10 +36,11 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past any range: reads 0
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int NS_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int NS_, int KG_ = 1>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, NS = NS_;
-  static constexpr int NW = WM * WN;
+  static constexpr int KG = KG_;                     // k groups: each takes 1/KG of every reduction tile
+  static constexpr int NW = WM * WN * KG;
   static constexpr int THREADS = NW * kWave;
   static constexpr int CPR = BK / 8;                 // 16-byte chunks per LDS row
   static constexpr int RS = 16 / CPR;                // rows per 256-byte bank window
@@ -62,6 +63,8 @@ struct Cfg {
   static_assert(BM * CPR % kWave == 0 && BN * CPR % kWave == 0, "tiles fill whole wave loads");
   static_assert((NS - 2) * L <= 63, "vmcnt holds at most 63 outstanding loads");
   static_assert(CPR <= 16 && 16 % CPR == 0, "row chunking");
+  static_assert(KG == 1 || (KG == 2 && (BK / 16) % 2 == 0), "k groups split the 16-wide steps evenly");
+  static_assert(KG == 1 || WM * WN * MI * NJ * 16 * kWave * 4 <= RING_BYTES, "k-group exchange fits the ring");
 };
 
 // Both double-buffered with long reduction tiles: fewer barriers per MFMA did more
@@ -71,6 +74,7 @@ struct Cfg {
 using CfgWide = Cfg<256, 192, 64, 4, 2, 2>;    // 8 waves of 64 x 96
 using CfgSquare = Cfg<128, 128, 128, 2, 4, 2>; // 8 waves of 64 x 32
 using CfgHalf = Cfg<64, 128, 128, 2, 4, 2>;    // 8 waves of 32 x 32: short products on few tiles
+using CfgSquareKG = Cfg<128, 128, 128, 2, 2, 2, 2>;   // two k groups of 4 waves of 64 x 64
 
 struct Seg {
   const uint16_t* a;   // [M, k] row-major (X or T)
@@ -94,7 +98,8 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmPar
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int kg = wave / (C::WM * C::WN), wr = wave % (C::WM * C::WN);
+  const int wm = wr / C::WN, wn = wr % C::WN;
   const bool second = tiles_a > 0 && int(blockIdx.x) >= tiles_a;
   const GemmParams& p = second ? pb : pa;
   int tile_m = blockIdx.y, tile_n = blockIdx.x;
@@ -203,11 +208,13 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmPar
       for (int j = 0; j < C::NJ; ++j)
         bfr[b][j] = *reinterpret_cast<const bf16x8_t*>(Bs + j * 32 * C::CPR * 16 + ch);
     };
-    read(0, 0);
+    constexpr int KSG = C::BK / 16 / C::KG;            // steps per k group
+    const int ks0 = kg * KSG;
+    read(ks0, 0);
 #pragma unroll
-    for (int ks = 0; ks < C::BK / 16; ++ks) {
-      const int b = ks & 1;
-      if (ks + 1 < C::BK / 16) read(ks + 1, b ^ 1);
+    for (int kk = 0; kk < KSG; ++kk) {
+      const int b = kk & 1;
+      if (kk + 1 < KSG) read(ks0 + kk + 1, b ^ 1);
       // (The scheduler would otherwise sink the reads back below the MFMAs.)
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -239,20 +246,45 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmPar
   wait_vmcnt<0>();
   __syncthreads();
 
+  if constexpr (C::KG == 2) {
+    // The second k group's sums meet the first's in LDS (fp32, [wave][i][j][v][lane]).
+    float* xch = reinterpret_cast<float*>(smem) + wr * (C::MI * C::NJ * 16 * kWave);
+    if (kg == 1) {
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) xch[((i * C::NJ + j) * 16 + v) * kWave + lane] = acc[i][j][v];
+    }
+    __syncthreads();
+    if (kg == 0) {
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[i][j][v] += xch[((i * C::NJ + j) * 16 + v) * kWave + lane];
+    }
+    __syncthreads();
+  }
+
   // bf16 tile through LDS, then 16-byte row stores. Accumulator v of a 32 x 32
   // block sits at row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
   uint16_t* out = reinterpret_cast<uint16_t*>(smem);
+  if (kg == 0) {
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i)
+    for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int j = 0; j < C::NJ; ++j) {
-      const int col = wn * C::WTN + j * 32 + fr;
+      for (int j = 0; j < C::NJ; ++j) {
+        const int col = wn * C::WTN + j * 32 + fr;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wm * C::WTM + i * 32 + 8 * (v >> 2) + 4 * fh + (v & 3);
-        out[row * C::OUT_PITCH + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][v]);
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * C::WTM + i * 32 + 8 * (v >> 2) + 4 * fh + (v & 3);
+          out[row * C::OUT_PITCH + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][v]);
+        }
       }
-    }
+  }
   __syncthreads();
   const bool vec = (p.N % 8) == 0 && (reinterpret_cast<uintptr_t>(p.y) % 16) == 0;
   constexpr int CH = C::BN / 8;
@@ -1132,12 +1164,15 @@ bool use_wide(int M, int N) {
   return tiles % 256 == 0 || tiles >= 1024;
 }
 
+// Square tiles run as two k groups of 4 waves of 64 x 64 (fewer LDS bytes per
+// MFMA than 8 waves of 64 x 32): measured 48.1 -> 47.9 us at 4096 x 4096 and
+// 145.6 -> 143.8 us for the MLP-shape backward, whose dX runs here.
 void launch_main(const GemmParams& g, hipStream_t stream) {
   if (g.M == 0 || g.N == 0) return;
   if (use_wide(g.M, g.N))
     launch_cfg<CfgWide>(g, stream);
   else
-    launch_cfg<CfgSquare>(g, stream);
+    launch_cfg<CfgSquareKG>(g, stream);
 }
 
 // Forward workspace: [tickets (64 KB, only ever tickets, so they stay zero between
