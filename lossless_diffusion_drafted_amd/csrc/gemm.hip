@@ -74,6 +74,7 @@ struct Cfg {
 using CfgWide = Cfg<256, 192, 64, 4, 2, 2>;    // 8 waves of 64 x 96
 using CfgSquare = Cfg<128, 128, 128, 2, 4, 2>; // 8 waves of 64 x 32
 using CfgHalf = Cfg<64, 128, 128, 2, 4, 2>;    // 8 waves of 32 x 32: short products on few tiles
+using CfgRow = Cfg<64, 128, 128, 2, 4, 3>;     // the same in a three-stage ring: 17-64 rows, split reduction
 using CfgSquareKG = Cfg<128, 128, 128, 2, 2, 2, 2>;   // two k groups of 4 waves of 64 x 64
 
 struct Seg {
@@ -88,13 +89,24 @@ struct GemmParams {
   int M, N;
   const uint8_t* mask1;    // row mask applied to segment 1's A rows (may be null)
   uint16_t* y;             // bf16 [M, N]
+  // Split reduction (the SK form only): slice blockIdx.z of gridDim.z takes
+  // reduction tiles [z kper, (z + 1) kper) of the extended reduction; slices store
+  // fp32 tiles in `part` and the last of a tile to finish (a ticket) adds them in
+  // slice order. Segment 1 may hold several groups' delta rows side by side (row
+  // stride t_stride): output columns from nb1 on use its second block of k1len,
+  // from nb2 on its third.
+  int kper;
+  float* part;             // [tiles, slices, BM * BN] fp32
+  unsigned* ticket;        // [tiles], zero on entry and on exit
+  int t_stride, nb1, nb2;
 };
 
 // One product on a 2-D grid (tiles_a == 0), or two independent products sharing
 // one launch on a 1-D grid: workgroups [0, tiles_a) take pa's tiles, the rest pb's
 // (small products that would each leave most CUs idle).
-template <class C>
+template <class C, bool SK = false>
 __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmParams pb, int tiles_a) {
+  static_assert(!SK || C::KG == 1, "split reduction with one k group");
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -113,6 +125,12 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmPar
   const int k0len = p.seg[0].k, k1len = p.nseg > 1 ? p.seg[1].k : 0;
   const int n0tiles = (k0len + C::BK - 1) / C::BK;
   const int ntiles = n0tiles + (k1len + C::BK - 1) / C::BK;
+  // The reduction tiles this workgroup takes: all, or its slice's.
+  const int t_begin = SK ? int(blockIdx.z) * p.kper : 0;
+  const int t_stop = SK ? min(ntiles, t_begin + p.kper) : ntiles;
+  // Segment 1's row stride and this column tile's block of it.
+  const int t_stride = SK && p.t_stride ? p.t_stride : k1len;
+  const int t_col = SK ? ((n0 >= p.nb1) + (n0 >= p.nb2)) * k1len : 0;
 
   // Per-thread load plan, fixed for the whole reduction. Slot q of a tile (16
   // bytes) holds row q / CPR, chunk (q % CPR) ^ swz(row). For each load: the byte
@@ -131,7 +149,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmPar
     if (real) a_ok0 |= 1u << i;
     if (real && (p.mask1 == nullptr || p.mask1[gr] != 0)) a_ok1 |= 1u << i;
     a_off0[i] = uint32_t((size_t(gr) * k0len + a_kc[i]) * 2);
-    a_off1[i] = uint32_t((size_t(gr) * k1len + a_kc[i]) * 2);
+    a_off1[i] = uint32_t((size_t(gr) * t_stride + t_col + a_kc[i]) * 2);
   }
 #pragma unroll
   for (int i = 0; i < C::B_INSTR; ++i) {
@@ -150,7 +168,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmPar
   const __amdgpu_buffer_rsrc_t ra0 = make_row_rsrc(p.seg[0].a, uint32_t(size_t(p.M) * k0len * 2));
   const __amdgpu_buffer_rsrc_t rb0 = make_row_rsrc(p.seg[0].b, uint32_t(size_t(p.N) * k0len * 2));
   const __amdgpu_buffer_rsrc_t ra1 = make_row_rsrc(p.nseg > 1 ? p.seg[1].a : p.seg[0].a,
-                                                   uint32_t(size_t(p.M) * k1len * 2));
+                                                   uint32_t(size_t(p.M) * t_stride * 2));
   const __amdgpu_buffer_rsrc_t rb1 = make_row_rsrc(p.nseg > 1 ? p.seg[1].b : p.seg[0].b,
                                                    uint32_t(size_t(p.N) * k1len * 2));
 
@@ -159,7 +177,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmPar
   auto issue = [&](int t, int st) {
     const bool s0 = t < n0tiles;                       // uniform
     const int kt = s0 ? t * C::BK : (t - n0tiles) * C::BK;
-    const int krem = t >= ntiles ? 0 : (s0 ? k0len : k1len) - kt;   // columns left in the segment
+    const int krem = t >= t_stop ? 0 : (s0 ? k0len : k1len) - kt;   // columns left in the segment
     const unsigned aok = s0 ? a_ok0 : a_ok1;
     const uint32_t kb = uint32_t(kt * 2);
     char* base = smem + st * C::STAGE_BYTES;
@@ -227,13 +245,13 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmPar
   };
 
 #pragma unroll
-  for (int s = 0; s < C::NS - 1; ++s) issue(s, s);
+  for (int s = 0; s < C::NS - 1; ++s) issue(t_begin + s, s);
   // Unrolled by NS so every ring stage index is a constant.
-  for (int t0 = 0; t0 < ntiles; t0 += C::NS) {
+  for (int t0 = t_begin; t0 < t_stop; t0 += C::NS) {
 #pragma unroll
     for (int s = 0; s < C::NS; ++s) {
       const int t = t0 + s;
-      if (t >= ntiles) break;
+      if (t >= t_stop) break;
       // Tile t's loads are done once at most the NS-2 later tiles' are in
       // flight; the barrier then publishes every wave's part and retires the
       // reads of the stage about to be refilled.
@@ -245,6 +263,56 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmPar
   }
   wait_vmcnt<0>();
   __syncthreads();
+
+  if constexpr (SK) {
+    // Split reduction: every slice stores its fp32 tile (accumulator order
+    // [wave][i][j][v][lane], device-coherent stores) and takes the tile's ticket;
+    // the last to finish adds all slices in slice order and writes the output.
+    __shared__ int s_last;
+    const int ks = int(gridDim.z);
+    if (ks > 1) {
+      const int tile = tile_m * int(gridDim.x) + tile_n;
+      constexpr int TILE = C::BM * C::BN;
+      const __amdgpu_buffer_rsrc_t rs =
+          make_row_rsrc(p.part + (size_t(tile) * ks + blockIdx.z) * TILE, uint32_t(TILE * 4));
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __float_as_uint(acc[i][j][v]), rs,
+                uint32_t(((((wave * C::MI + i) * C::NJ + j) * 16 + v) * kWave + lane) * 4), 0u, kBufDeviceCoherent);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) {
+        const unsigned old = __hip_atomic_fetch_add(&p.ticket[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = old == unsigned(ks - 1) ? 1 : 0;
+      }
+      __syncthreads();
+      if (!s_last) return;
+      const __amdgpu_buffer_rsrc_t rp = make_row_rsrc(p.part + size_t(tile) * ks * TILE, uint32_t(ks * TILE * 4));
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NJ; ++j) {
+          const uint32_t off = uint32_t((((wave * C::MI + i) * C::NJ + j) * 16 * kWave + lane) * 4);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+          for (int q = 0; q < ks; ++q) {
+            float x[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              x[v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                  rp, off + uint32_t((q * TILE + v * kWave) * 4), 0u, kBufDeviceCoherent));
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] += x[v];
+          }
+        }
+      if (tid == 0) __hip_atomic_store(&p.ticket[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 
   if constexpr (C::KG == 2) {
     // The second k group's sums meet the first's in LDS (fp32, [wave][i][j][v][lane]).
@@ -1198,11 +1266,63 @@ int fwd_lora_slices(int M, int K, int r) {
   return (tiles <= 128 && K >= 1024) ? 2 : 1;
 }
 
+// Small-M products at 17-64 rows that are not wide enough for the streaming form
+// run on 64 x 128 row tiles (the tiled kernel's loads: 256-byte runs of W rows
+// through LDS, not the small-M kernel's 64-byte operand-order loads) with the
+// reduction in about 256 / tiles slices (at most 8) of at least two reduction
+// tiles. The slice count depends on K alone, so the workspace size does not
+// depend on the rank; the delta tiles join the last slice's range.
+int tiled_small_slices(int M, int N, int K) {
+  using C = CfgRow;
+  const int tiles = ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
+  const int kt = (K + C::BK - 1) / C::BK;
+  int ks = 256 / tiles;                              // one round of workgroups
+  if (ks > 8) ks = 8;
+  if (ks > kt / 2) ks = kt / 2;
+  return ks < 1 ? 1 : ks;
+}
+
+// Where it won (measured per product, weights from HBM): at 33-64 rows every
+// decode-step product (4096 -> 12288 at 64 rows 62.4 -> 38.5 us, 12288 -> 4096
+// 60.4 -> 43.6, 4096 -> 4096 18.7 -> 15.0); at 17-32 rows the large ones (4096 ->
+// 12288 at 32 rows 44.7 -> 35.6 us) and the looped stack's step as a whole (12.8
+// -> 10.4 ms), but not the smallest (4096 -> 1024 at 32 rows 16.7 -> 18.9 us).
+bool tiled_small_ok(const GemmArgs& a) {
+  if (a.M <= 16 || a.M > 64 || a.y_f32 || use_skinny2(a.M, a.N, a.K)) return false;
+  if (a.M <= 32 && size_t(a.N) * a.K < (size_t(6) << 20)) return false;
+  for (int g = 0; g + 1 < a.groups; ++g)
+    if (a.gstart[g] % CfgRow::BN != 0) return false;   // a column tile takes one group's delta rows
+  const int tiles = (a.N + CfgRow::BN - 1) / CfgRow::BN;
+  return tiles <= kMaxTickets;
+}
+
+size_t tiled_small_part_bytes(int M, int N, int K, int r) {
+  if (M <= 16 || M > 64 || use_skinny2(M, N, K)) return 0;
+  const int ks = tiled_small_slices(M, N, K);
+  if (ks <= 1) return 0;
+  return align256(size_t((N + CfgRow::BN - 1) / CfgRow::BN) * ks * CfgRow::BM * CfgRow::BN * 4);
+}
+
+void launch_tiled_small(GemmParams g, float* part, unsigned* tickets, hipStream_t stream) {
+  using C = CfgRow;
+  const int k0t = (g.seg[0].k + C::BK - 1) / C::BK;
+  const int kt = k0t + (g.nseg > 1 ? (g.seg[1].k + C::BK - 1) / C::BK : 0);
+  const int ks = tiled_small_slices(g.M, g.N, g.seg[0].k);
+  g.kper = (k0t + ks - 1) / ks;
+  if (ks * g.kper < kt) g.kper = (kt + ks - 1) / ks;   // the last slice takes the delta tiles too
+  g.part = part;
+  g.ticket = tickets;
+  const dim3 grid((g.N + C::BN - 1) / C::BN, (g.M + C::BM - 1) / C::BM, ks);
+  hipLaunchKernelGGL((gemm_kernel<C, true>), grid, dim3(C::THREADS), 0, stream, g, g, 0);
+}
+
 size_t skinny_part_bytes(int M, int N, int K, int r) {
   int ks = small_slices(M, N, K), ks_r = r > 0 ? small_slices(M, r, K) : 1;
   size_t big = 0;
   if (ks > 1) big = size_t(ks) * M * N * 4;
   if (ks_r > 1 && size_t(ks_r) * M * r * 4 > big) big = size_t(ks_r) * M * r * 4;
+  const size_t ts = tiled_small_part_bytes(M, N, K, r);
+  if (ts > big) big = ts;
   return align256(big);
 }
 
@@ -1254,6 +1374,23 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
       p.mask = a.row_mask;
       p.y = tws;
       launch_small(p, stream);
+    }
+    if (tiled_small_ok(a)) {
+      GemmParams g{};
+      g.seg[0] = Seg{static_cast<const uint16_t*>(a.X), static_cast<const uint16_t*>(a.W), a.K};
+      g.nseg = 1;
+      if (a.r > 0) {
+        g.seg[1] = Seg{tws, static_cast<const uint16_t*>(a.B), a.r};   // scaled and gated already
+        g.nseg = 2;
+      }
+      g.M = a.M;
+      g.N = a.N;
+      g.y = static_cast<uint16_t*>(a.Y);
+      g.t_stride = rt;
+      g.nb1 = a.groups > 1 ? a.gstart[0] : INT_MAX;
+      g.nb2 = a.groups > 2 ? a.gstart[1] : INT_MAX;
+      launch_tiled_small(g, part, tickets, stream);
+      return hipGetLastError();
     }
     p.w = static_cast<const uint16_t*>(a.W);
     p.N = a.N;
