@@ -1235,12 +1235,50 @@ bool use_wide(int M, int N) {
 // Square tiles run as two k groups of 4 waves of 64 x 64 (fewer LDS bytes per
 // MFMA than 8 waves of 64 x 32): measured 48.1 -> 47.9 us at 4096 x 4096 and
 // 145.6 -> 143.8 us for the MLP-shape backward, whose dX runs here.
-void launch_main(const GemmParams& g, hipStream_t stream) {
+// Products whose square tiles fill less than half the CUs (the looped stack's
+// 2560-wide projections at 512 rows: 80 tiles) split the reduction into up to 8
+// slices so about 256 workgroups run, each at least three reduction tiles long;
+// the last slice of a tile adds the fp32 slice tiles in slice order.
+struct SplitPlan {
+  int ks;
+  size_t part_bytes;
+};
+SplitPlan split_plan(int M, int N, int k0, int k1) {
+  using C = CfgSquare;
+  const int tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+  const int kt = (k0 + C::BK - 1) / C::BK + (k1 + C::BK - 1) / C::BK;
+  SplitPlan s{1, 0};
+  if (use_wide(M, N) || tiles >= 128 || tiles > 16384) return s;
+  int ks = 256 / tiles;
+  if (ks > 8) ks = 8;
+  if (ks > kt / 3) ks = kt / 3;
+  if (ks < 2) return s;
+  const int kper = (kt + ks - 1) / ks;
+  s.ks = (kt + kper - 1) / kper;
+  s.part_bytes = align256(size_t(tiles) * s.ks * C::BM * C::BN * 4);
+  return s;
+}
+
+void launch_main(const GemmParams& g, hipStream_t stream, float* part = nullptr, unsigned* tickets = nullptr) {
   if (g.M == 0 || g.N == 0) return;
-  if (use_wide(g.M, g.N))
+  if (use_wide(g.M, g.N)) {
     launch_cfg<CfgWide>(g, stream);
-  else
-    launch_cfg<CfgSquareKG>(g, stream);
+    return;
+  }
+  const SplitPlan sp = split_plan(g.M, g.N, g.seg[0].k, g.nseg > 1 ? g.seg[1].k : 0);
+  if (sp.ks > 1 && part && tickets) {
+    using C = CfgSquare;
+    GemmParams gs = g;
+    const int kt = (g.seg[0].k + C::BK - 1) / C::BK + (g.nseg > 1 ? (g.seg[1].k + C::BK - 1) / C::BK : 0);
+    gs.kper = (kt + sp.ks - 1) / sp.ks;
+    gs.part = part;
+    gs.ticket = tickets;
+    gs.nb1 = gs.nb2 = INT_MAX;
+    const dim3 grid((g.N + C::BN - 1) / C::BN, (g.M + C::BM - 1) / C::BM, sp.ks);
+    hipLaunchKernelGGL((gemm_kernel<C, true>), grid, dim3(C::THREADS), 0, stream, gs, gs, 0);
+    return;
+  }
+  launch_cfg<CfgSquareKG>(g, stream);
 }
 
 // Forward workspace: [tickets (64 KB, only ever tickets, so they stay zero between
@@ -1334,7 +1372,9 @@ size_t gemm_workspace_bytes(int M, int N, int K, int r) {
   // One region serves whichever path runs: the small-M slice tiles or the
   // LoRA-down's slice tiles.
   const size_t sk = (M <= 64 && K % SK_GROUP == 0 && r % 32 == 0) ? skinny_part_bytes(M, N, K, r) : 0;
-  const size_t ld = r > 0 ? align256(size_t((M + 31) / 32) * ((r + 31) / 32) * LD_MAX_SLICES * 1024 * 4) : 0;
+  size_t ld = r > 0 ? align256(size_t((M + 31) / 32) * ((r + 31) / 32) * LD_MAX_SLICES * 1024 * 4) : 0;
+  const size_t sp = split_plan(M, N, K, r).part_bytes;   // the main product's slice tiles (after the LoRA-down)
+  if (sp > ld) ld = sp;
   return n + (sk > ld ? sk : ld);
 }
 
@@ -1422,7 +1462,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   g.M = a.M;
   g.N = a.N;
   g.y = static_cast<uint16_t*>(a.Y);
-  launch_main(g, stream);
+  launch_main(g, stream, part, tickets);
   return hipGetLastError();
 }
 
@@ -1455,7 +1495,8 @@ size_t bwd_part_bytes(int M, int N, int K, int r) {
   size_t n = 0;
   if (jt.ks > 1) n += size_t(jt.tiles) * jt.ks * 1024 * 4;
   if (ju.ks > 1) n += size_t(ju.tiles) * ju.ks * 1024 * 4;
-  return align256(n);
+  const size_t dx = split_plan(M, K, N, r).part_bytes;     // dX's slice tiles, after the LoRA-down
+  return align256(n > dx ? n : dx);
 }
 BwdWs bwd_ws(void* ws, int M, int N, int K, int r) {
   char* c = static_cast<char*>(ws);
@@ -1542,7 +1583,7 @@ hipError_t launch_gemm_bwd(const GemmBwdArgs& a, hipStream_t stream) {
     g.M = M;
     g.N = K;
     g.y = static_cast<uint16_t*>(a.dX);
-    launch_main(g, stream);
+    launch_main(g, stream, w.part, w.tickets);   // the LoRA-down's slices are done with both
   }
   // 4. dA = U^T X (rows of U^T against rows of X^T, reduction over M) and dB =
   //    (diag(m) dY)^T (s T), one launch.
