@@ -134,6 +134,17 @@ class KernelTimer:
         self.pairs = {}
 
 
+def settle(fn, ms=30.0):
+    """Run fn back to back for about ms milliseconds: the measurement that follows
+    sees the clock of a busy GPU (from idle the clock takes about 25 ms to ramp)."""
+    import torch
+    t_end = time.perf_counter() + ms / 1000.0
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
 def median_us_flushed(fn, n, flush):
     """Median time of n single calls, each with its own HIP event pair on the launch
     stream, after a write of the whole `flush` buffer (512 MB: larger than L2 and the
@@ -594,9 +605,7 @@ def tv_benchmark(uno, workloads, dev, iters):
         if e.status != "UNO_ERR_UNSUPPORTED":
             raise
         return {"status": "not built"}
-    for _ in range(2):
-        uno.uno_tv_loss_fwd_bwd(t, s, mask, c["temperature"], want_rows=False)
-    torch.cuda.synchronize()
+    settle(lambda: uno.uno_tv_loss_fwd_bwd(t, s, mask, c["temperature"], want_rows=False), 40.0)
     n_resp = int(mask.sum().item())
     timer = KernelTimer()
     timer.run("tv", lambda: uno.uno_tv_loss_fwd_bwd(t, s, mask, c["temperature"], want_rows=False), iters)
@@ -626,11 +635,10 @@ def lora_bwd_benchmark(uno, workloads, dev, iters):
         Wt = W.t().contiguous()          # the frozen weight, transposed once (setup, not timed)
         f_w = lambda: uno.uno_gated_lora_linear_bwd(G, X, W, A, B, mask, 1.0)
         f_wt = lambda: uno.uno_gated_lora_linear_bwd(G, X, W, A, B, mask, 1.0, W_t=Wt)
-        f_w()
-        f_wt()
-        torch.cuda.synchronize()
+        settle(f_w)
         timer = KernelTimer()
         timer.run("w", f_w, iters)
+        settle(f_wt)
         timer.run("b", f_wt, iters)
         torch.cuda.synchronize()
         ms = timer.avg_ms("b")
@@ -667,8 +675,7 @@ def verify_sweep(uno, workloads, p_np, q_np, dev, iters):
             fn = lambda: uno.uno_verify_block(p, q, draft, seq, pos, want_slot_accept=False, want_diag=False,
                                               out=outs, **sp)
             timer = KernelTimer()
-            fn()
-            torch.cuda.synchronize()
+            settle(fn)
             timer.run("v", fn, iters)
             torch.cuda.synchronize()
             ms = timer.avg_ms("v")
@@ -701,8 +708,7 @@ def verify_leg(uno, workloads, name, dev, iters, flush):
                 resampled=torch.empty((S,), dtype=torch.int32, device=dev))
     fn = lambda: uno.uno_verify_block(p, q, draft, seq, pos, want_slot_accept=False, want_diag=False,
                                       out=outs, **sp)
-    fn()
-    torch.cuda.synchronize()
+    settle(fn)
     timer = KernelTimer()
     timer.run("v", fn, iters)
     torch.cuda.synchronize()
@@ -732,8 +738,7 @@ def gemm_leg(uno, workloads, name, dev, iters, flush):
         X, W, A, B = (dev_tensor(a, dev) for a in workloads.gemm_inputs(M, K, N, r, tag=gi))
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         fn = lambda: uno.uno_gated_lora_linear(X, W, A, B, mask, 1.0, out=Y)
-        fn()
-        torch.cuda.synchronize()
+        settle(fn)
         timer = KernelTimer()
         timer.run("g", fn, iters)
         torch.cuda.synchronize()
