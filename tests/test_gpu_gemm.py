@@ -203,3 +203,30 @@ def test_row_tile_shapes(M, K, N, r):
     rows = None if M * N * K <= 2e9 else np.random.default_rng(1).choice(M, 96, replace=False)
     print(f"tiled gated LoRA M={M} K={K} N={N} r={r}", flush=True)
     _check_case(M, K, N, r, 16.0, mask, rows=rows)
+
+
+def test_two_streams_with_their_own_workspaces():
+    """Calls on two streams at once, each stream with its own workspace (the binding
+    keeps one per stream): the split-reduction forms' tickets and slice tiles live in
+    the workspace, so the results must equal the same calls made one at a time."""
+    shapes = [(512, 2560, 2560, 64),    # square tiles with the reduction in slices
+              (64, 4096, 4096, 128),    # row tiles at 64 rows, slices
+              (1024, 4096, 4096, 128)]  # LoRA-down in two slices
+    runs = []
+    for M, K, N, r in shapes:
+        X, W, A, B = workloads.gemm_inputs(M, K, N, r, seed=11)
+        runs.append(([to_device(a, DEV) for a in (X, W, A, B)], to_device(workloads.noise_row_mask(M // 8, 8), DEV)))
+    ref = [_bits(_run(*args, mask, 2.0)) for args, mask in runs]
+    streams = [torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)]
+    outs = [[None] * len(runs) for _ in streams]
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for si, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                for i in (range(len(runs)) if si == 0 else reversed(range(len(runs)))):
+                    args, mask = runs[i]
+                    outs[si][i] = _uno().uno_gated_lora_linear(*args, mask, 2.0)
+        torch.cuda.synchronize()
+        for si in range(len(streams)):
+            for i in range(len(runs)):
+                np.testing.assert_array_equal(_bits(outs[si][i]), ref[i])

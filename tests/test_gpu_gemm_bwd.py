@@ -176,3 +176,37 @@ def test_backward_alternating_shapes_share_the_workspace():
         for run, ref in zip(reversed(runs), reversed(first)):
             for a, b in zip(once(*run), ref):
                 assert torch.equal(a, b)
+
+
+def test_backward_on_two_streams():
+    """Backward calls on two streams at once, each with its own workspace: the
+    LoRA-down slice counters and dX's slice tiles live in the workspace, so results
+    equal the same calls made one at a time."""
+    shapes = [(512, 2560, 2560, 64), (256, 1024, 3072, 32)]
+    runs = []
+    for M, K, N, r in shapes:
+        X, W, A, B = workloads.gemm_inputs(M, K, N, r, seed=12)
+        G = workloads.gemm_grad(M, N, seed=12)
+        runs.append(([to_device(a, DEV) for a in (G, X, W, A, B)], to_device(workloads.noise_row_mask(M // 8, 8), DEV)))
+
+    def call(run):
+        args, mask = run
+        return _uno().uno_gated_lora_linear_bwd(*args, mask, 4.0)
+
+    ref = []
+    for run in runs:
+        out = call(run)
+        torch.cuda.synchronize()
+        ref.append([t.view(torch.int16).cpu() for t in out])
+    streams = [torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)]
+    for rep in range(3):
+        outs = [[None] * len(runs) for _ in streams]
+        for si, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                for i in (range(len(runs)) if si == 0 else reversed(range(len(runs)))):
+                    outs[si][i] = call(runs[i])
+        torch.cuda.synchronize()
+        for si in range(len(streams)):
+            for i in range(len(runs)):
+                for a, b in zip(outs[si][i], ref[i]):
+                    assert torch.equal(a.view(torch.int16).cpu(), b)
