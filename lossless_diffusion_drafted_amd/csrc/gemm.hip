@@ -99,11 +99,18 @@ struct GemmParams {
   float* part;             // [tiles, slices, BM * BN] fp32
   unsigned* ticket;        // [tiles], zero on entry and on exit
   int t_stride, nb1, nb2;
+  // Segment 0's A rows gathered by heads (the SK form, BK = 128): with x_group > 0
+  // the rows are x_stride apart and reduction tile t reads source tile t / x_group.
+  int x_stride, x_group;
 };
 
 // One product on a 2-D grid (tiles_a == 0), or two independent products sharing
 // one launch on a 1-D grid: workgroups [0, tiles_a) take pa's tiles, the rest pb's
 // (small products that would each leave most CUs idle).
+// floor(t / d) = (t * gather_mul(d)) >> 20 for t * d < 2^20: with m = ceil(2^20 /
+// d) = (2^20 + e) / d, 0 <= e < d, the error term t * e / (d 2^20) stays below 1 / d.
+__device__ inline unsigned gather_mul(int d) { return d > 0 ? ((1u << 20) + unsigned(d) - 1) / unsigned(d) : 0u; }
+
 template <class C, bool SK = false>
 __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmParams pb, int tiles_a) {
   static_assert(!SK || C::KG == 1, "split reduction with one k group");
@@ -131,6 +138,10 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmPar
   // Segment 1's row stride and this column tile's block of it.
   const int t_stride = SK && p.t_stride ? p.t_stride : k1len;
   const int t_col = SK ? ((n0 >= p.nb1) + (n0 >= p.nb2)) * k1len : 0;
+  const int x_group = SK ? p.x_group : 0;
+  const int x_stride = x_group > 0 ? p.x_stride : k0len;
+  const unsigned x_mul = gather_mul(x_group);
+  static_assert(!SK || C::BK == 128, "the gather maps whole 128-wide reduction tiles");
 
   // Per-thread load plan, fixed for the whole reduction. Slot q of a tile (16
   // bytes) holds row q / CPR, chunk (q % CPR) ^ swz(row). For each load: the byte
@@ -148,7 +159,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmPar
     const bool real = i * C::NW + wave < C::A_WI && gr < p.M;
     if (real) a_ok0 |= 1u << i;
     if (real && (p.mask1 == nullptr || p.mask1[gr] != 0)) a_ok1 |= 1u << i;
-    a_off0[i] = uint32_t((size_t(gr) * k0len + a_kc[i]) * 2);
+    a_off0[i] = uint32_t((size_t(gr) * x_stride + a_kc[i]) * 2);
     a_off1[i] = uint32_t((size_t(gr) * t_stride + t_col + a_kc[i]) * 2);
   }
 #pragma unroll
@@ -165,7 +176,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmPar
   // vmcnt arithmetic of the ring counts only the tile loads.
   wait_vmcnt<0>();
 
-  const __amdgpu_buffer_rsrc_t ra0 = make_row_rsrc(p.seg[0].a, uint32_t(size_t(p.M) * k0len * 2));
+  const __amdgpu_buffer_rsrc_t ra0 = make_row_rsrc(p.seg[0].a, uint32_t(size_t(p.M) * x_stride * 2));
   const __amdgpu_buffer_rsrc_t rb0 = make_row_rsrc(p.seg[0].b, uint32_t(size_t(p.N) * k0len * 2));
   const __amdgpu_buffer_rsrc_t ra1 = make_row_rsrc(p.nseg > 1 ? p.seg[1].a : p.seg[0].a,
                                                    uint32_t(size_t(p.M) * t_stride * 2));
@@ -175,26 +186,72 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(GemmParams pa, GemmPar
   // Issue the loads of reduction tile t into ring stage st. Tiles past the end
   // load out of range (zeros), so every step issues exactly L loads.
   auto issue = [&](int t, int st) {
-    const bool s0 = t < n0tiles;                       // uniform
-    const int kt = s0 ? t * C::BK : (t - n0tiles) * C::BK;
-    const int krem = t >= t_stop ? 0 : (s0 ? k0len : k1len) - kt;   // columns left in the segment
-    const unsigned aok = s0 ? a_ok0 : a_ok1;
-    const uint32_t kb = uint32_t(kt * 2);
-    char* base = smem + st * C::STAGE_BYTES;
+    if constexpr (!SK) {
+      const bool s0 = t < n0tiles;                       // uniform
+      const int kt = s0 ? t * C::BK : (t - n0tiles) * C::BK;
+      const int krem = t >= t_stop ? 0 : (s0 ? k0len : k1len) - kt;   // columns left in the segment
+      const unsigned aok = s0 ? a_ok0 : a_ok1;
+      const uint32_t kb = uint32_t(kt * 2);
+      char* base = smem + st * C::STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < C::A_INSTR; ++i) {
-      const bool ok = ((aok >> i) & 1u) && a_kc[i] < krem;
-      const uint32_t off = ok ? (s0 ? a_off0[i] : a_off1[i]) + kb : kOutOfRange;
-      char* dst = i * C::NW + wave < C::A_WI ? base + (i * C::NW + wave) * 1024 : smem + C::DUMMY_OFF;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(s0 ? ra0 : ra1, (lds_ptr_t)dst, 16, off, 0, 0, 0);
-    }
+      for (int i = 0; i < C::A_INSTR; ++i) {
+        const bool ok = ((aok >> i) & 1u) && a_kc[i] < krem;
+        const uint32_t off = ok ? (s0 ? a_off0[i] : a_off1[i]) + kb : kOutOfRange;
+        char* dst = i * C::NW + wave < C::A_WI ? base + (i * C::NW + wave) * 1024 : smem + C::DUMMY_OFF;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s0 ? ra0 : ra1, (lds_ptr_t)dst, 16, off, 0, 0, 0);
+      }
 #pragma unroll
-    for (int i = 0; i < C::B_INSTR; ++i) {
-      const bool ok = ((b_ok >> i) & 1u) && b_kc[i] < krem;
-      const uint32_t off = ok ? (s0 ? b_off0[i] : b_off1[i]) + kb : kOutOfRange;
-      char* dst = i * C::NW + wave < C::B_WI ? base + C::A_BYTES + (i * C::NW + wave) * 1024
-                                             : smem + C::DUMMY_OFF;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(s0 ? rb0 : rb1, (lds_ptr_t)dst, 16, off, 0, 0, 0);
+      for (int i = 0; i < C::B_INSTR; ++i) {
+        const bool ok = ((b_ok >> i) & 1u) && b_kc[i] < krem;
+        const uint32_t off = ok ? (s0 ? b_off0[i] : b_off1[i]) + kb : kOutOfRange;
+        char* dst = i * C::NW + wave < C::B_WI ? base + C::A_BYTES + (i * C::NW + wave) * 1024
+                                               : smem + C::DUMMY_OFF;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s0 ? rb0 : rb1, (lds_ptr_t)dst, 16, off, 0, 0, 0);
+      }
+    } else {
+      // Each segment in a branch of its own (the segment is uniform): selecting
+      // between the two segments' offset arrays per load would put them in
+      // scratch memory here.
+      char* base = smem + st * C::STAGE_BYTES;
+      const bool s0 = t < n0tiles;
+      const int kt = (s0 ? t : t - n0tiles) * C::BK;
+      const int krem = t >= t_stop ? 0 : (s0 ? k0len : k1len) - kt;   // columns left in the segment
+      const uint32_t kb = uint32_t(kt * 2);
+      if (s0) {
+        // gathered rows: X's tile t is tile t / x_group of the source
+        const uint32_t akb = x_group > 0 ? ((unsigned(t) * x_mul) >> 20) * (C::BK * 2) : kb;
+#pragma unroll
+        for (int i = 0; i < C::A_INSTR; ++i) {
+          const bool ok = ((a_ok0 >> i) & 1u) && a_kc[i] < krem;
+          const uint32_t off = ok ? a_off0[i] + akb : kOutOfRange;
+          char* dst = i * C::NW + wave < C::A_WI ? base + (i * C::NW + wave) * 1024 : smem + C::DUMMY_OFF;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra0, (lds_ptr_t)dst, 16, off, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < C::B_INSTR; ++i) {
+          const bool ok = ((b_ok >> i) & 1u) && b_kc[i] < krem;
+          const uint32_t off = ok ? b_off0[i] + kb : kOutOfRange;
+          char* dst = i * C::NW + wave < C::B_WI ? base + C::A_BYTES + (i * C::NW + wave) * 1024
+                                                 : smem + C::DUMMY_OFF;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb0, (lds_ptr_t)dst, 16, off, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::A_INSTR; ++i) {
+          const bool ok = ((a_ok1 >> i) & 1u) && a_kc[i] < krem;
+          const uint32_t off = ok ? a_off1[i] + kb : kOutOfRange;
+          char* dst = i * C::NW + wave < C::A_WI ? base + (i * C::NW + wave) * 1024 : smem + C::DUMMY_OFF;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra1, (lds_ptr_t)dst, 16, off, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < C::B_INSTR; ++i) {
+          const bool ok = ((b_ok >> i) & 1u) && b_kc[i] < krem;
+          const uint32_t off = ok ? b_off1[i] + kb : kOutOfRange;
+          char* dst = i * C::NW + wave < C::B_WI ? base + C::A_BYTES + (i * C::NW + wave) * 1024
+                                                 : smem + C::DUMMY_OFF;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb1, (lds_ptr_t)dst, 16, off, 0, 0, 0);
+        }
+      }
     }
   };
 
@@ -619,6 +676,9 @@ struct SkinnyParams {
   // t_stride); columns from nb1 on use T's second block of r, from nb2 on its
   // third (INT_MAX: one group).
   int t_stride, nb1, nb2;
+  // X gathered by heads (x_group > 0): X row m at x_stride elements apart, its
+  // 128-wide group g read from source group g / x_group.
+  int x_stride, x_group;
   float scale;            // epilogue: y = mask[m] ? scale * acc : 0 (mask may be null)
   const uint8_t* mask;
   uint16_t* y;            // [M, N] bf16
@@ -647,7 +707,9 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
   const int g0 = int((long long)G * wi / nw), g1 = int((long long)G * (wi + 1) / nw);
   const int fr = lane & 15, fg = lane >> 4;
 
-  const __amdgpu_buffer_rsrc_t rx = make_row_rsrc(p.x, uint32_t(size_t(p.M) * p.K * 2));
+  const int xs = p.x_group > 0 ? p.x_stride : p.K;        // X row stride
+  const unsigned x_mul = gather_mul(p.x_group);
+  const __amdgpu_buffer_rsrc_t rx = make_row_rsrc(p.x, uint32_t(size_t(p.M) * xs * 2));
   const __amdgpu_buffer_rsrc_t rw = make_row_rsrc(p.w, uint32_t(size_t(p.N) * p.K * 2));
   uint32_t xo[MB], wo[NB];
   bool xin[MB], win[NB];
@@ -655,7 +717,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
   for (int i = 0; i < MB; ++i) {
     const int m = i * 16 + fr;
     xin[i] = m < p.M;
-    xo[i] = uint32_t((size_t(m) * p.K + fg * 8) * 2);
+    xo[i] = uint32_t((size_t(m) * xs + fg * 8) * 2);
   }
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
@@ -675,6 +737,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
   // every call issues the same loads and the waits are counted at compile time.
   auto load = [&](int g, u32x4_t (&xv)[MB][4], u32x4_t (&wv)[NB][4]) {
     const uint32_t kb = uint32_t(g) * SK_GROUP * 2;
+    const uint32_t xkb = p.x_group > 0 ? ((unsigned(g) * x_mul) >> 20) * (SK_GROUP * 2) : kb;
     const bool live = g < g1;
 #pragma unroll
     for (int j = 0; j < NB; ++j)
@@ -686,7 +749,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
     for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        xv[i][c] = __builtin_amdgcn_raw_buffer_load_b128(rx, (live && xin[i]) ? xo[i] + kb + c * 64 : kOutOfRange,
+        xv[i][c] = __builtin_amdgcn_raw_buffer_load_b128(rx, (live && xin[i]) ? xo[i] + xkb + c * 64 : kOutOfRange,
                                                          0u, 0);
   };
   auto mma = [&](const u32x4_t (&xv)[MB][4], const u32x4_t (&wv)[NB][4]) {
@@ -1378,6 +1441,17 @@ size_t gemm_workspace_bytes(int M, int N, int K, int r) {
   return n + (sk > ld ? sk : ld);
 }
 
+bool gemm_gathers_x(const GemmArgs& a) {
+  // the gathered X exists on the small-M path's one-pass kernels only
+  const int rt = a.r * a.groups;
+  const bool small = skinny_ok(a.M, a.N, a.K, a.r, a.X, a.W, a.A, a.B) &&
+                     (a.N + SK_COLS - 1) / SK_COLS <= kMaxTickets && (rt + SK_COLS - 1) / SK_COLS <= kMaxTickets;
+  return a.x_group > 0 && small && !use_skinny2(a.M, a.N, a.K) && !use_skinny2(a.M, rt, a.K) &&
+         (a.K / SK_GROUP) % a.x_group == 0 && size_t(a.K / SK_GROUP) * a.x_group < (size_t(1) << 20) &&
+         a.x_stride >= a.K / a.x_group &&
+         size_t(a.M) * a.x_stride * 2 < (size_t(1) << 32);
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   char* ws = static_cast<char*>(a.ws);
@@ -1393,10 +1467,13 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
                      (a.N + SK_COLS - 1) / SK_COLS <= kMaxTickets && (rt + SK_COLS - 1) / SK_COLS <= kMaxTickets;
   if (a.y_f32 && !small) return hipErrorInvalidValue;   // fp32 output exists on the small-M path only
   if (a.groups < 1 || a.groups > 3 || (a.groups > 1 && !small)) return hipErrorInvalidValue;
+  if (a.x_group < 0 || (a.x_group > 0 && !gemm_gathers_x(a))) return hipErrorInvalidValue;
   if (small) {
     SkinnyParams p{};
     p.M = a.M;
     p.K = a.K;
+    p.x_stride = a.x_stride;
+    p.x_group = a.x_group;
     p.part = part;
     p.ticket = tickets;
     p.x = static_cast<const uint16_t*>(a.X);
@@ -1429,6 +1506,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
       g.t_stride = rt;
       g.nb1 = a.groups > 1 ? a.gstart[0] : INT_MAX;
       g.nb2 = a.groups > 2 ? a.gstart[1] : INT_MAX;
+      g.x_stride = a.x_stride;
+      g.x_group = a.x_group;
       launch_tiled_small(g, part, tickets, stream);
       return hipGetLastError();
     }

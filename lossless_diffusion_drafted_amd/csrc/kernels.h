@@ -73,6 +73,12 @@ struct GemmArgs {
   // are multiples of 32. The workspace is sized for rank groups * r.
   int groups = 1;
   int gstart[2] = {0, 0};
+  // X gathered by heads (small-M path only): with x_group > 0, X row m is read from
+  // rows x_stride elements apart, and its 128-column block h (a head of width 128)
+  // from source block h / x_group: X = the heads of a one-token attention output
+  // expanded from their shared kv heads. K must be a multiple of 128.
+  int x_stride = 0;
+  int x_group = 0;
 };
 
 size_t verify_workspace_bytes(int S, int b);
@@ -87,6 +93,8 @@ int tv_max_vocab(bool bf16);          // largest V one row team covers on this d
 hipError_t launch_tv(const TvArgs& a, hipStream_t stream);
 size_t gemm_workspace_bytes(int M, int N, int K, int r);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+// Whether launch_gemm takes these arguments' X gathered by heads (x_group > 0).
+bool gemm_gathers_x(const GemmArgs& a);
 
 struct GemmBwdArgs {
   const void* dY;

@@ -218,8 +218,8 @@ size_t fwd_bytes(const ModelDesc& md, int M) {
 // Projection `proj` of a layer, or with n > 1 the n projections proj .. proj + n -
 // 1 as one grouped product (their weights, and adapter factors, stacked in memory;
 // `cols` gives each one's output width).
-hipError_t gated(const ModelDesc& md, int layer, int proj, const uint16_t* x, uint16_t* y, int M, int K,
-                 const int* cols, int n, const uint8_t* mask, unsigned* tickets, void* scratch, hipStream_t st) {
+GemmArgs gated_args(const ModelDesc& md, int layer, int proj, const uint16_t* x, uint16_t* y, int M, int K,
+                    const int* cols, int n, const uint8_t* mask, unsigned* tickets, void* scratch) {
   GemmArgs g{};
   g.X = x;
   g.W = md.w[layer * 7 + proj];
@@ -240,7 +240,12 @@ hipError_t gated(const ModelDesc& md, int layer, int proj, const uint16_t* x, ui
   g.groups = n;
   g.ws = scratch;
   g.tickets = tickets;
-  return launch_gemm(g, st);
+  return g;
+}
+
+hipError_t gated(const ModelDesc& md, int layer, int proj, const uint16_t* x, uint16_t* y, int M, int K,
+                 const int* cols, int n, const uint8_t* mask, unsigned* tickets, void* scratch, hipStream_t st) {
+  return launch_gemm(gated_args(md, layer, proj, x, y, M, K, cols, n, mask, tickets, scratch), st);
 }
 
 // Whether projections proj .. proj + n - 1 of a layer can run as one grouped
@@ -290,9 +295,19 @@ hipError_t forward(const ModelDesc& md, const int32_t* tokens, const uint8_t* ma
         if ((e = gated(md, l, 1, f.x, f.k, M, H, kcol, 1, mask, tickets, f.gemm, st)) != hipSuccess) break;
         if ((e = gated(md, l, 2, f.x, f.v, M, H, kcol, 1, mask, tickets, f.gemm, st)) != hipSuccess) break;
       }
-      hipLaunchKernelGGL(expand_kernel, dim3(eg < 4096 ? eg : 4096), dim3(MT), 0, st, v, vstride, f.a, M, H, KVW,
-                         md.head_dim);
-      if ((e = gated(md, l, 3, f.a, f.o, M, H, hcol, 1, mask, tickets, f.gemm, st)) != hipSuccess) break;
+      // The o-projection's input: each query head's attention output is its kv
+      // head's value row. With 128-wide heads the small-M product reads those
+      // blocks from v itself; otherwise they are copied out first.
+      GemmArgs og = gated_args(md, l, 3, v, f.o, M, H, hcol, 1, mask, tickets, f.gemm);
+      og.x_stride = vstride;
+      og.x_group = md.head_dim == 128 ? H / KVW : 0;
+      if (og.x_group == 0 || !gemm_gathers_x(og)) {
+        hipLaunchKernelGGL(expand_kernel, dim3(eg < 4096 ? eg : 4096), dim3(MT), 0, st, v, vstride, f.a, M, H, KVW,
+                           md.head_dim);
+        og.X = f.a;
+        og.x_stride = og.x_group = 0;
+      }
+      if ((e = launch_gemm(og, st)) != hipSuccess) break;
       hipLaunchKernelGGL(norm_kernel, dim3(M), dim3(MT), 0, st, nullptr, nullptr, 0, f.h, f.o, f.x, H);
       if (stacked(md, l, 4, gu_cols, 2, H, lora)) {
         if ((e = gated(md, l, 4, f.x, f.gu, M, H, gu_cols, 2, mask, tickets, f.gemm, st)) != hipSuccess) break;

@@ -49,10 +49,17 @@ def _uno():
 _MODELS = {}
 
 
+def _config(name):
+    """A reduced stack's sizes; small_hd64 is the small stack with 64-wide heads."""
+    if name == "small_hd64":
+        return dict(workloads.STEP_CONFIGS["small"], head_dim=64)
+    return workloads.STEP_CONFIGS[name]
+
+
 def _models(name):
     """(host model as bf16 bits, device Model) for a reduced stack."""
     if name not in _MODELS:
-        c = workloads.STEP_CONFIGS[name]
+        c = _config(name)
         host = workloads.step_model_host(c, seed=1)
         _MODELS[name] = (host, _device_model(host, c))
     return _MODELS[name]
@@ -86,18 +93,20 @@ def _inputs(S, V, seed):
     return seed_tok, seq, pos
 
 
-@pytest.mark.parametrize("name,loops,stacked", [("small", 1, True), ("small_looped", 2, True),
-                                                ("small", 1, False)])
-def test_forward_matches_oracle(name, loops, stacked):
+@pytest.mark.parametrize("name,loops,stacked,M", [("small", 1, True, 40), ("small_looped", 2, True, 40),
+                                                  ("small", 1, False, 40), ("small", 1, True, 8),
+                                                  ("small_hd64", 1, True, 40)])
+def test_forward_matches_oracle(name, loops, stacked, M):
     """Logits of the forward against the oracle's, with the grouped q | k | v and
-    gate | up products (stacked weights) and without them."""
+    gate | up products (stacked weights) and without them. The o-projection reads
+    its 128-wide heads straight from v (8 rows: one-pass kernel; 40: row tiles;
+    kv groups of 4 and of 1) and 64-wide heads from an expanded copy."""
     uno = _uno()
     host, model = _models(name)
     if not stacked:
-        model = _device_model(host, workloads.STEP_CONFIGS[name], stacked=False)
+        model = _device_model(host, _config(name), stacked=False)
     V = host["embed"].shape[0]
     rng = np.random.default_rng(5)
-    M = 40
     toks = rng.integers(0, V, M).astype(np.int32)
     mask = (rng.random(M) < 0.6).astype(np.uint8)
     z = uno.uno_forward(model, to_device(toks, DEV), to_device(mask, DEV), loops=loops)
