@@ -1072,14 +1072,32 @@ void launch_skinny2(const SkinnyParams& p, hipStream_t stream) {
 }
 
 // K slices of a small-M product: about one workgroup per CU (measured best
-// against 2, 4 and 8 per CU), each wave at least one 128-wide group.
+// against 2, 4 and 8 per CU), each wave at least one 128-wide group. Then the
+// count whose workgroups spread most evenly over the 256 CUs: time goes as
+// ceil(tiles ks / 256) / ks, the most workgroups one CU runs times each one's
+// share of the reduction. Fewer slices are taken when that is lower (80 column
+// tiles: 3 slices, 240 workgroups, not 4 and 320); more only when it is lower by
+// 5% and each wave keeps at least 2.5 groups (640 tiles: 2 slices, not 1;
+// 192 tiles stay at 2, as 4 slices of 2 groups a wave measured slower).
 int skinny_slices(int N, int K) {
   const int tiles = (N + SK_COLS - 1) / SK_COLS;
   const int G = K / SK_GROUP;
-  int ks = (256 + tiles - 1) / tiles;
   int cap = G / 4 > 1 ? G / 4 : 1;
   if (cap > SK_MAX_SLICES) cap = SK_MAX_SLICES;
-  return ks < cap ? ks : cap;
+  int ks = (256 + tiles - 1) / tiles;
+  if (ks > cap) ks = cap;
+  int best = ks;
+  long bn = (long(tiles) * ks + 255) / 256, bd = ks;   // the cost bn / bd of the best so far
+  for (int k = 1; k <= cap; ++k) {
+    if (k > ks && 2 * G < 5 * 4 * k) break;
+    const long n = (long(tiles) * k + 255) / 256;
+    if (k < ks ? n * bd < bn * k : 20 * n * bd < 19 * bn * k) {
+      best = k;
+      bn = n;
+      bd = k;
+    }
+  }
+  return best;
 }
 
 bool skinny_ok(int M, int N, int K, int r, const void* x, const void* w, const void* a, const void* b) {
