@@ -75,6 +75,7 @@ using CfgWide = Cfg<256, 192, 64, 4, 2, 2>;    // 8 waves of 64 x 96
 using CfgSquare = Cfg<128, 128, 128, 2, 4, 2>; // 8 waves of 64 x 32
 using CfgHalf = Cfg<64, 128, 128, 2, 4, 2>;    // 8 waves of 32 x 32: short products on few tiles
 using CfgRow = Cfg<64, 128, 128, 2, 4, 3>;     // the same in a three-stage ring: 17-64 rows, split reduction
+using CfgRow96 = Cfg<64, 96, 128, 2, 3, 3>;    // 6 waves of 32 x 32: the same on 96-wide column tiles
 using CfgSquareKG = Cfg<128, 128, 128, 2, 2, 2, 2>;   // two k groups of 4 waves of 64 x 64
 
 struct Seg {
@@ -1386,19 +1387,44 @@ int fwd_lora_slices(int M, int K, int r) {
 }
 
 // Small-M products at 17-64 rows that are not wide enough for the streaming form
-// run on 64 x 128 row tiles (the tiled kernel's loads: 256-byte runs of W rows
-// through LDS, not the small-M kernel's 64-byte operand-order loads) with the
-// reduction in about 256 / tiles slices (at most 8) of at least two reduction
-// tiles. The slice count depends on K alone, so the workspace size does not
-// depend on the rank; the delta tiles join the last slice's range.
+// run on 64-row tiles (the tiled kernel's loads: 256-byte runs of W rows through
+// LDS, not the small-M kernel's 64-byte operand-order loads) with the reduction
+// in about 256 / tiles slices (at most 8) of at least two reduction tiles. The
+// slice count depends on K alone, so the workspace size does not depend on the
+// rank; the delta tiles join the last slice's range.
+template <class C>
 int tiled_small_slices(int M, int N, int K) {
-  using C = CfgRow;
   const int tiles = ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
   const int kt = (K + C::BK - 1) / C::BK;
   int ks = 256 / tiles;                              // one round of workgroups
   if (ks > 8) ks = 8;
   if (ks > kt / 2) ks = kt / 2;
   return ks < 1 ? 1 : ks;
+}
+
+// Workgroups per CU-slot of the launch on C's tiles (1: every CU busy in every round).
+template <class C>
+double tiled_small_fill(int M, int N, int K) {
+  const long w = long((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM) * tiled_small_slices<C>(M, N, K);
+  return double(w) / (256.0 * double((w + 255) / 256));
+}
+
+// Whether C's column tiles fit the groups: each group boundary on a tile boundary.
+template <class C>
+bool groups_align(const GemmArgs& a) {
+  for (int g = 0; g + 1 < a.groups; ++g)
+    if (a.gstart[g] % C::BN != 0) return false;   // a column tile reads one group's delta rows
+  return (a.N + C::BN - 1) / C::BN <= kMaxTickets;
+}
+
+// Column tiles of 128, or of 96 where those fill the CUs better (gate | up at
+// 24576 columns: 256 tiles of 96 against 192 of 128, 75% of the CUs). 0: neither
+// fits the groups.
+int row_tile_bn(const GemmArgs& a) {
+  const bool ok128 = groups_align<CfgRow>(a), ok96 = groups_align<CfgRow96>(a);
+  if (ok96 && (!ok128 || tiled_small_fill<CfgRow96>(a.M, a.N, a.K) > tiled_small_fill<CfgRow>(a.M, a.N, a.K) + 0.05))
+    return 96;
+  return ok128 ? 128 : 0;
 }
 
 // Where it won (measured per product, weights from HBM): at 33-64 rows every
@@ -1409,30 +1435,40 @@ int tiled_small_slices(int M, int N, int K) {
 bool tiled_small_ok(const GemmArgs& a) {
   if (a.M <= 16 || a.M > 64 || a.y_f32 || use_skinny2(a.M, a.N, a.K)) return false;
   if (a.M <= 32 && size_t(a.N) * a.K < (size_t(6) << 20)) return false;
-  for (int g = 0; g + 1 < a.groups; ++g)
-    if (a.gstart[g] % CfgRow::BN != 0) return false;   // a column tile takes one group's delta rows
-  const int tiles = (a.N + CfgRow::BN - 1) / CfgRow::BN;
-  return tiles <= kMaxTickets;
+  return row_tile_bn(a) != 0;
 }
 
+template <class C>
+size_t tiled_small_part_bytes_c(int M, int N, int K) {
+  const int ks = tiled_small_slices<C>(M, N, K);
+  if (ks <= 1) return 0;
+  return align256(size_t((N + C::BN - 1) / C::BN) * ks * C::BM * C::BN * 4);
+}
+
+// Either tile width's slice tiles (the groups, which pick it, are not known here).
 size_t tiled_small_part_bytes(int M, int N, int K, int r) {
   if (M <= 16 || M > 64 || use_skinny2(M, N, K)) return 0;
-  const int ks = tiled_small_slices(M, N, K);
-  if (ks <= 1) return 0;
-  return align256(size_t((N + CfgRow::BN - 1) / CfgRow::BN) * ks * CfgRow::BM * CfgRow::BN * 4);
+  return std::max(tiled_small_part_bytes_c<CfgRow>(M, N, K), tiled_small_part_bytes_c<CfgRow96>(M, N, K));
 }
 
-void launch_tiled_small(GemmParams g, float* part, unsigned* tickets, hipStream_t stream) {
-  using C = CfgRow;
+template <class C>
+void launch_tiled_small_c(GemmParams g, float* part, unsigned* tickets, hipStream_t stream) {
   const int k0t = (g.seg[0].k + C::BK - 1) / C::BK;
   const int kt = k0t + (g.nseg > 1 ? (g.seg[1].k + C::BK - 1) / C::BK : 0);
-  const int ks = tiled_small_slices(g.M, g.N, g.seg[0].k);
+  const int ks = tiled_small_slices<C>(g.M, g.N, g.seg[0].k);
   g.kper = (k0t + ks - 1) / ks;
   if (ks * g.kper < kt) g.kper = (kt + ks - 1) / ks;   // the last slice takes the delta tiles too
   g.part = part;
   g.ticket = tickets;
   const dim3 grid((g.N + C::BN - 1) / C::BN, (g.M + C::BM - 1) / C::BM, ks);
   hipLaunchKernelGGL((gemm_kernel<C, true>), grid, dim3(C::THREADS), 0, stream, g, g, 0);
+}
+
+void launch_tiled_small(const GemmParams& g, int bn, float* part, unsigned* tickets, hipStream_t stream) {
+  if (bn == 96)
+    launch_tiled_small_c<CfgRow96>(g, part, tickets, stream);
+  else
+    launch_tiled_small_c<CfgRow>(g, part, tickets, stream);
 }
 
 size_t skinny_part_bytes(int M, int N, int K, int r) {
@@ -1526,7 +1562,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
       g.nb2 = a.groups > 2 ? a.gstart[1] : INT_MAX;
       g.x_stride = a.x_stride;
       g.x_group = a.x_group;
-      launch_tiled_small(g, part, tickets, stream);
+      launch_tiled_small(g, row_tile_bn(a), part, tickets, stream);
       return hipGetLastError();
     }
     p.w = static_cast<const uint16_t*>(a.W);
