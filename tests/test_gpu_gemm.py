@@ -98,6 +98,9 @@ def test_ragged_shapes(M, K, N, r):
     (1, 128, 32, 32),          # one row, one reduction group, one column tile
     (4, 4096, 4096, 0),        # an AR step's rows on a 4096-wide projection (frozen)
     (4, 4096, 1024, 128),
+    (4, 4096, 24576, 128),     # gate | up at an AR step's rows: 768 workgroups, one slice
+    (8, 1024, 32768 + 64, 32), # more than 1024 workgroups, ragged columns
+    (3, 3584, 8192 + 8, 32),   # seven groups a wave (an odd count), ragged columns
     (16, 2560, 2560, 64),
     (17, 512, 100, 32),        # ragged rows and columns
     (32, 2560, 10240, 64),     # four sequences x block 8 (looped model shapes)
