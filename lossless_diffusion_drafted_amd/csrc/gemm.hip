@@ -1378,11 +1378,15 @@ void launch_small(const SkinnyParams& p, hipStream_t stream) {
 }
 
 // Reduction slices of the forward's LoRA-down on the tiled path: two when the
-// tiles alone would leave CUs idle and their tickets fit the ticket area.
+// tiles alone would leave CUs idle and their tickets fit the ticket area, four
+// when they fill a quarter of the CUs at most and the reduction is long.
 // (Measured at the Qwen shapes, 128 tiles: two slices 1.8 us faster per call than
-// one; three and four, which take a second round of workgroups, 4-6 us slower.)
+// one; three and four, which take a second round of workgroups, 4-6 us slower.
+// At the looped stack's 512 rows and rank 64, 32 tiles: the seven projections in
+// 315.8 us with two slices, 305.1 with four, 304.3 with eight.)
 int fwd_lora_slices(int M, int K, int r) {
   const int tiles = ((M + 31) / 32) * ((r + 31) / 32);
+  if (tiles <= 64 && K >= 2048) return 4;
   return (tiles <= 128 && K >= 1024) ? 2 : 1;
 }
 
