@@ -77,6 +77,7 @@ using CfgHalf = Cfg<64, 128, 128, 2, 4, 2>;    // 8 waves of 32 x 32: short prod
 using CfgRow = Cfg<64, 128, 128, 2, 4, 3>;     // the same in a three-stage ring: 17-64 rows, split reduction
 using CfgRow96 = Cfg<64, 96, 128, 2, 3, 3>;    // 6 waves of 32 x 32: the same on 96-wide column tiles
 using CfgSquareKG = Cfg<128, 128, 128, 2, 2, 2, 2>;   // two k groups of 4 waves of 64 x 64
+using CfgSq160 = Cfg<128, 160, 128, 4, 1, 2, 2>;   // two k groups of 4 waves of 32 x 160
 
 struct Seg {
   const uint16_t* a;   // [M, k] row-major (X or T)
@@ -1341,6 +1342,20 @@ SplitPlan split_plan(int M, int N, int k0, int k1) {
   return s;
 }
 
+// Share of the CU slots the launch's rounds of workgroups fill (one workgroup per CU).
+double round_fill(long tiles) { return double(tiles) / (256.0 * double((tiles + 255) / 256)); }
+
+// 128 x 160 tiles where their rounds fill the CUs clearly better than square ones:
+// the looped stack's gate and up (512 rows, 2560 -> 10240) are 320 square tiles, a
+// quarter of the CUs taking a second, or 256 tiles of 160 columns in one round.
+// Measured there: the seven projections 305 -> 270 us. The same tiles as 5 waves of
+// 128 x 32 (one SIMD holding two of them), as 4 waves of 32 x 160, or with 64-wide
+// reduction tiles in three stages: 272-274 us.
+bool use_sq160(int M, int N) {
+  const long rows = (M + 127) / 128;
+  return round_fill(rows * ((N + 159) / 160)) > round_fill(rows * ((N + 127) / 128)) + 0.1;
+}
+
 void launch_main(const GemmParams& g, hipStream_t stream, float* part = nullptr, unsigned* tickets = nullptr) {
   if (g.M == 0 || g.N == 0) return;
   if (use_wide(g.M, g.N)) {
@@ -1358,6 +1373,10 @@ void launch_main(const GemmParams& g, hipStream_t stream, float* part = nullptr,
     gs.nb1 = gs.nb2 = INT_MAX;
     const dim3 grid((g.N + C::BN - 1) / C::BN, (g.M + C::BM - 1) / C::BM, sp.ks);
     hipLaunchKernelGGL((gemm_kernel<C, true>), grid, dim3(C::THREADS), 0, stream, gs, gs, 0);
+    return;
+  }
+  if (use_sq160(g.M, g.N)) {
+    launch_cfg<CfgSq160>(g, stream);
     return;
   }
   launch_cfg<CfgSquareKG>(g, stream);

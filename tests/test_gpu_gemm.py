@@ -89,6 +89,7 @@ def test_tiny_gated_lora(scale):
     (300, 1000, 72, 0),       # r = 0: plain linear
     (512, 2560, 640, 64),
     (100, 2056, 200, 40),     # LoRA-down in four reduction slices, the last one short
+    (500, 264, 10200, 16),    # 128 x 160 tiles (256 of them, not 320 square), ragged
 ])
 def test_ragged_shapes(M, K, N, r):
     mask = (np.random.default_rng(M * N).random(M) < 0.8).astype(np.uint8)
