@@ -90,6 +90,7 @@ def test_tiny_gated_lora(scale):
     (512, 2560, 640, 64),
     (100, 2056, 200, 40),     # LoRA-down in four reduction slices, the last one short
     (500, 264, 10200, 16),    # 128 x 160 tiles (256 of them, not 320 square), ragged
+    (4096, 1000, 4080, 24),   # 256 x 256 tiles (one round), ragged columns and reduction
 ])
 def test_ragged_shapes(M, K, N, r):
     mask = (np.random.default_rng(M * N).random(M) < 0.8).astype(np.uint8)
