@@ -75,6 +75,8 @@ def test_tiny_backward(scale):
     (136, 2560, 10240, 64),    # looped-model MLP shape, few rows
     (200, 1000, 3000, 24),     # U's reduction in 3 slices, the last one short
     (96, 3072, 1024, 40),      # T's reduction in 3 slices, a partial column tile
+    (504, 10200, 264, 16),     # dX on 128 x 160 tiles, ragged
+    (4096, 4080, 1000, 24),    # dX on 256 x 256 tiles (one round), ragged columns
 ])
 def test_ragged_backward(M, K, N, r):
     mask = (np.random.default_rng(M + N).random(M) < 0.8).astype(np.uint8)
